@@ -1,0 +1,193 @@
+/*
+ * svgear.h — C ABI of the MI355X (gfx950) routed sparse-attention library.
+ *
+ * The library computes the hot path of SVG-EAR ("SVG-EAR: Parameter-Free
+ * Linear Compensation for Sparse Video Generation via Error-aware Routing",
+ * arXiv 2603.08982) for one attention layer:
+ *
+ *   svgear_cluster   k-means of each head's Q rows or K rows      (paper §4.1)
+ *   svgear_permute   stable cluster-contiguous permutation + means (§3.1, §4.1, §4.3)
+ *   svgear_probe     query-centroid error probe -> block ratios    (§4.2, Eq. 5)
+ *   svgear_route     greedy error-to-cost selection per query cluster (§4.2, §5)
+ *   svgear_attend    exact selected blocks + centroid compensation (§4.1, §4.3)
+ *   svgear_unpermute inverse permutation of the output rows        (§3.1)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are DEVICE pointers, row-major, head-major: X[h][n][j] at
+ *    X + (h*N + n)*d + j. Index arrays are int32 device pointers.
+ *  - svgear_dtype names the element type of Q/K/V-like tensors: SVGEAR_F32
+ *    (float) or SVGEAR_BF16 (bfloat16 stored as uint16). Centroid tables,
+ *    ratios and normalisers are always float32.
+ *  - Supported head dimension d: 64 or 128. Cluster counts: 1 <= C <= min(N, 1024).
+ *  - Ownership: the caller allocates and frees every buffer, including the
+ *    workspace; the library never allocates, frees or synchronises. Work is
+ *    enqueued on the caller's stream `s` (0 = the legacy default stream) and
+ *    every buffer must stay valid until that work has completed.
+ *  - Errors: argument problems are reported synchronously, before anything
+ *    is enqueued (SVGEAR_ERR_INVALID_ARG, SVGEAR_ERR_UNSUPPORTED,
+ *    SVGEAR_ERR_WORKSPACE). A failed kernel launch returns SVGEAR_ERR_HIP.
+ *    Faults inside kernels surface at the caller's next synchronisation, as
+ *    for any asynchronous HIP work.
+ *  - Calls hold no state between invocations and may be made from several
+ *    host threads on different streams; two calls that share an output or a
+ *    workspace buffer must be ordered by the caller.
+ *  - Results are deterministic: the same inputs give bitwise identical
+ *    outputs (no floating-point atomics).
+ */
+#ifndef SVGEAR_H
+#define SVGEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* svgear_stream_t; /* same object as hipStream_t */
+
+typedef enum {
+  SVGEAR_OK = 0,
+  SVGEAR_ERR_INVALID_ARG = 1, /* null pointer, size out of range, inconsistent sizes */
+  SVGEAR_ERR_UNSUPPORTED = 2, /* dtype or head dimension not built */
+  SVGEAR_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace() */
+  SVGEAR_ERR_HIP = 4          /* the HIP runtime refused a launch */
+} svgear_status;
+
+typedef enum { SVGEAR_F32 = 0, SVGEAR_BF16 = 1 } svgear_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* svgear_status_string(svgear_status st);
+
+/* Bytes of workspace svgear_cluster needs for H heads of N rows, dimension d,
+ * C clusters, element type dt. Returns 0 for arguments svgear_cluster would reject. */
+size_t svgear_cluster_workspace(svgear_dtype dt, int H, int N, int d, int C);
+
+/*
+ * k-means clustering of every head's rows (paper §4.1: Q and K are clustered
+ * into C_q and C_k clusters).
+ *
+ * Runs `iters` (>= 1) Lloyd iterations from the caller's initial centroids:
+ * each row goes to the centroid with the smallest squared Euclidean distance
+ * (ties to the lowest index), then every centroid with members becomes their
+ * mean; a centroid without members keeps its value. The distance is formed
+ * from the centroid rounded to the input element type (bf16 or f32),
+ * accumulated in f32; means are accumulated in f32 in a fixed order.
+ *
+ *   X         [H][N][d] dt, input rows.
+ *   centroids [H][C][d] f32, in: initial centroids; out: means of the final labels
+ *             (empty clusters keep their last value).
+ *   labels    [H][N] int32 out: cluster of every row from the last assignment.
+ *   counts    [H][C] int32 out: members per cluster under those labels.
+ *   ws        device workspace of at least svgear_cluster_workspace(...) bytes.
+ */
+svgear_status svgear_cluster(svgear_dtype dt, int H, int N, int d, int C, int iters,
+                             const void* X, float* centroids, int32_t* labels, int32_t* counts,
+                             void* ws, size_t ws_bytes, svgear_stream_t s);
+
+/* Bytes of workspace svgear_permute needs. */
+size_t svgear_permute_workspace(svgear_dtype dt, int H, int N, int d, int C);
+
+/*
+ * Stable permutation that lays every cluster out contiguously (paper §3.1),
+ * applied to one or two tensors that share the labels, with the mean row of
+ * every cluster (the centroids q-bar, k-bar and mean values v-bar of §4.1/§4.3;
+ * V takes K's labels).
+ *
+ *   labels    [H][N] int32 in, each in [0, C) (values outside are clamped into
+ *             that range, so no access leaves its buffer).
+ *   perm      [H][N] int32 out: perm[p] = source row placed in slot p; rows of
+ *             one cluster keep their original order.
+ *   offsets   [H][C+1] int32 out: cluster c occupies slots offsets[c]..offsets[c+1]-1.
+ *   ntensors  1 or 2.
+ *   src       host array of ntensors device pointers, [H][N][d] dt each.
+ *   dst       host array of ntensors device pointers, [H][N][d] dt each (permuted
+ *             rows: dst[p] = src[perm[p]]); must not alias src.
+ *   means     host array of ntensors device pointers, [H][C][d] f32 each, or NULL
+ *             entries to skip; empty clusters get a zero row. `means` itself may be NULL.
+ */
+svgear_status svgear_permute(svgear_dtype dt, int H, int N, int d, int C, const int32_t* labels,
+                             int32_t* perm, int32_t* offsets, int ntensors,
+                             const void* const* src, void* const* dst, float* const* means,
+                             void* ws, size_t ws_bytes, svgear_stream_t s);
+
+/* Bytes of workspace svgear_probe needs. */
+size_t svgear_probe_workspace(int H, int Nk, int Cq, int Ck);
+
+/*
+ * Query-centroid error probe (paper §4.2, Eq. 5) and block error-to-size ratio.
+ *
+ * For query centroid c and permuted key j of key cluster k(j), with
+ * s = scale*qbar_c.k_j, s~ = scale*qbar_c.kbar_k(j), m_c = max_j s and
+ * Z_c = sum_j exp(s - m_c):
+ *     eps_cj = (exp(s - m_c) - exp(s~ - m_c)) / Z_c
+ *     ratio[c][c'] = (1/|k_c'|) * sum_{j in c'} eps_cj^2      (-1 if |k_c'| = 0)
+ *     log_norm[c]  = m_c + ln Z_c
+ * The logits are formed from q-bar split into a bf16 high part and a bf16
+ * remainder (about 16 significant bits) against the bf16 or f32 keys, f32 accumulation.
+ *
+ *   q_centroids [H][Cq][d] f32;  Kp [H][Nk][d] dt (permuted keys);
+ *   k_centroids [H][Ck][d] f32;  k_offsets [H][Ck+1] int32 (offsets[Ck] = Nk);
+ *   ratio       [H][Cq][Ck] f32 out;  log_norm [H][Cq] f32 out, may be NULL.
+ */
+svgear_status svgear_probe(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck, float scale,
+                           const float* q_centroids, const void* Kp, const float* k_centroids,
+                           const int32_t* k_offsets, float* ratio, float* log_norm, void* ws,
+                           size_t ws_bytes, svgear_stream_t s);
+
+/*
+ * Greedy error-to-cost routing per query cluster (paper §4.2 "Error
+ * estimation", §5 "Implementation": routing at query-cluster granularity).
+ *
+ * For every (head, query cluster): non-empty key clusters are ordered by
+ * ratio, highest first, equal ratios by lower index; walking that order once,
+ * a key cluster is selected when its keys still fit in `budget_keys` (clusters
+ * that do not fit are passed over; later, smaller ones may still fit).
+ * budget_keys = floor(rho * Nk) is computed by the caller.
+ *
+ *   ratio     [H][Cq][Ck] f32 in (>= 0 for non-empty clusters; the value of
+ *             empty clusters is ignored).
+ *   k_offsets [H][Ck+1] int32 in.
+ *   sel_mask  [H][Cq][Ck] uint8 out (1 = exact).
+ *   sel_list  [H][Cq][Ck] int32 out: selected key clusters ascending, -1 padded. May be NULL.
+ *   sel_count [H][Cq] int32 out: number selected. May be NULL.
+ *   sel_keys  [H][Cq] int32 out: exact keys used (<= budget_keys). May be NULL.
+ */
+svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int32_t* k_offsets,
+                           int32_t budget_keys, uint8_t* sel_mask, int32_t* sel_list,
+                           int32_t* sel_count, int32_t* sel_keys, svgear_stream_t s);
+
+/*
+ * Compensated block-sparse attention on permuted Q, K, V (paper §4.1 block
+ * mask, §4.3 linear compensation).
+ *
+ * Query i of query cluster c gets one softmax over (a) scale*q_i.k_j for every
+ * key j of every key cluster c' with sel_mask[c][c'] = 1, value v_j, and (b) for
+ * every other non-empty key cluster c', scale*q_i.kbar_c' + ln|k_c'| with value
+ * vbar_c'. QK^T and PV run on bf16 (or f32) matrix cores with f32 accumulation;
+ * the softmax is f32; for bf16 the probabilities and the centroid rows are
+ * rounded to bf16 as matrix operands.
+ *
+ *   Qp [H][Nq][d], Kp/Vp [H][Nk][d] dt;  q_offsets [H][Cq+1], k_offsets [H][Ck+1];
+ *   k_centroids, v_centroids [H][Ck][d] f32;  sel_mask [H][Cq][Ck] uint8;
+ *   Op [H][Nq][d] dt out (rows in the permuted query order).
+ */
+svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
+                            float scale, const void* Qp, const void* Kp, const void* Vp,
+                            const int32_t* q_offsets, const int32_t* k_offsets,
+                            const float* k_centroids, const float* v_centroids,
+                            const uint8_t* sel_mask, void* Op, svgear_stream_t s);
+
+/*
+ * Inverse permutation of output rows: X[h][perm[h][p]] = Xp[h][p] (paper §3.1).
+ *   perm [H][N] int32 (a permutation of 0..N-1 per head); Xp, X [H][N][d] dt, not aliased.
+ */
+svgear_status svgear_unpermute(svgear_dtype dt, int H, int N, int d, const int32_t* perm,
+                               const void* Xp, void* X, svgear_stream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVGEAR_H */

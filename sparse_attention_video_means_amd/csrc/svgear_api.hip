@@ -1,0 +1,207 @@
+// C ABI of libsvgear: argument validation, workspace carving and launches.
+// Every entry point checks all of its arguments before it enqueues anything,
+// never allocates or synchronises, and returns the first launch error.
+#include <hip/hip_runtime.h>
+
+#include "../../include/svgear.h"
+#include "svgear_internal.hpp"
+
+using namespace svg;
+
+namespace {
+
+int elem_bytes(svgear_dtype dt) {
+  return dt == SVGEAR_BF16 ? 2 : (dt == SVGEAR_F32 ? 4 : 0);
+}
+
+bool dim_ok(int d) { return d == 64 || d == 128; }
+
+// Common shape check for a tensor family clustered into C clusters.
+svgear_status check_shape(svgear_dtype dt, int H, int N, int d, int C) {
+  if (H < 1 || N < 1 || C < 1 || C > N || C > kMaxClusters) return SVGEAR_ERR_INVALID_ARG;
+  if (elem_bytes(dt) == 0 || !dim_ok(d)) return SVGEAR_ERR_UNSUPPORTED;
+  if (size_t(H) * N * d > (size_t(1) << 40)) return SVGEAR_ERR_INVALID_ARG;
+  return SVGEAR_OK;
+}
+
+hipStream_t as_stream(svgear_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+struct ClusterWs {
+  SortWs sort;
+  int32_t* perm;
+  int32_t* offsets;
+  void* table;
+  float* norms;
+};
+
+size_t cluster_ws_bytes(int eb, int H, int N, int d, int C) {
+  return sort_ws_bytes(H, N, d, C, 1) + align256(sizeof(int32_t) * size_t(H) * N) +
+         align256(sizeof(int32_t) * size_t(H) * (C + 1)) + align256(size_t(eb) * H * C * d) +
+         align256(sizeof(float) * size_t(H) * C);
+}
+
+ClusterWs cluster_ws_carve(void* ws, int eb, int H, int N, int d, int C) {
+  ClusterWs w;
+  w.sort = sort_ws_carve(ws, H, N, d, C, 1);
+  char* p = static_cast<char*>(ws) + sort_ws_bytes(H, N, d, C, 1);
+  w.perm = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * size_t(H) * N);
+  w.offsets = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * size_t(H) * (C + 1));
+  w.table = p;
+  p += align256(size_t(eb) * H * C * d);
+  w.norms = reinterpret_cast<float*>(p);
+  return w;
+}
+
+size_t probe_ws_bytes(int H, int Nk, int Cq, int Ck) {
+  return align256(sizeof(int32_t) * size_t(H) * (Ck + 1)) +
+         align256(sizeof(float) * 3 * size_t(H) * max_units(Nk, Ck) * Cq);
+}
+
+#define SVG_TRY(expr)                                      \
+  do {                                                     \
+    if ((expr) != hipSuccess) return SVGEAR_ERR_HIP;       \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* svgear_status_string(svgear_status st) {
+  switch (st) {
+    case SVGEAR_OK: return "ok";
+    case SVGEAR_ERR_INVALID_ARG: return "invalid argument";
+    case SVGEAR_ERR_UNSUPPORTED: return "unsupported dtype or head dimension";
+    case SVGEAR_ERR_WORKSPACE: return "workspace too small";
+    case SVGEAR_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+size_t svgear_cluster_workspace(svgear_dtype dt, int H, int N, int d, int C) {
+  if (check_shape(dt, H, N, d, C) != SVGEAR_OK) return 0;
+  return cluster_ws_bytes(elem_bytes(dt), H, N, d, C);
+}
+
+svgear_status svgear_cluster(svgear_dtype dt, int H, int N, int d, int C, int iters,
+                             const void* X, float* centroids, int32_t* labels, int32_t* counts,
+                             void* ws, size_t ws_bytes, svgear_stream_t s) {
+  const svgear_status st = check_shape(dt, H, N, d, C);
+  if (st != SVGEAR_OK) return st;
+  if (iters < 1 || !X || !centroids || !labels || !counts) return SVGEAR_ERR_INVALID_ARG;
+  const int eb = elem_bytes(dt);
+  if (!ws || ws_bytes < cluster_ws_bytes(eb, H, N, d, C)) return SVGEAR_ERR_WORKSPACE;
+  const hipStream_t hs = as_stream(s);
+  ClusterWs w = cluster_ws_carve(ws, eb, H, N, d, C);
+  SVG_TRY(launch_table(eb, H, d, C, centroids, w.table, w.norms, hs));
+  for (int it = 0; it < iters; ++it) {
+    SVG_TRY(launch_assign(eb, H, N, d, C, X, w.table, w.norms, labels, w.sort.rank, w.sort.hist, hs));
+    SVG_TRY(launch_sort_scan(H, N, C, w.sort.hist, w.offsets, counts, w.sort.chunk_prefix, hs));
+    SVG_TRY(launch_scatter(labels, w.sort.rank, w.sort.hist, H, N, C, w.perm, hs));
+    const void* src[1] = {X};
+    SVG_TRY(launch_segsum(eb, H, N, d, C, w.perm, w.offsets, w.sort.chunk_prefix, 1, src, nullptr,
+                          w.sort.partial, hs));
+    float* means[1] = {centroids};
+    const bool last = it + 1 == iters;
+    SVG_TRY(launch_combine(eb, H, d, C, 1, w.offsets, w.sort.chunk_prefix, w.sort.partial, N, means,
+                           /*mode=*/1, last ? nullptr : w.table, w.norms, hs));
+  }
+  return SVGEAR_OK;
+}
+
+size_t svgear_permute_workspace(svgear_dtype dt, int H, int N, int d, int C) {
+  if (check_shape(dt, H, N, d, C) != SVGEAR_OK) return 0;
+  return sort_ws_bytes(H, N, d, C, 2);
+}
+
+svgear_status svgear_permute(svgear_dtype dt, int H, int N, int d, int C, const int32_t* labels,
+                             int32_t* perm, int32_t* offsets, int ntensors,
+                             const void* const* src, void* const* dst, float* const* means,
+                             void* ws, size_t ws_bytes, svgear_stream_t s) {
+  const svgear_status st = check_shape(dt, H, N, d, C);
+  if (st != SVGEAR_OK) return st;
+  if (!labels || !perm || !offsets || ntensors < 1 || ntensors > 2 || !src || !dst)
+    return SVGEAR_ERR_INVALID_ARG;
+  for (int k = 0; k < ntensors; ++k)
+    if (!src[k] || !dst[k] || src[k] == dst[k]) return SVGEAR_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < sort_ws_bytes(H, N, d, C, 2)) return SVGEAR_ERR_WORKSPACE;
+  const int eb = elem_bytes(dt);
+  const hipStream_t hs = as_stream(s);
+  SortWs w = sort_ws_carve(ws, H, N, d, C, 2);
+  SVG_TRY(launch_label_rank(labels, H, N, C, w.rank, w.hist, hs));
+  SVG_TRY(launch_sort_scan(H, N, C, w.hist, offsets, nullptr, w.chunk_prefix, hs));
+  SVG_TRY(launch_scatter(labels, w.rank, w.hist, H, N, C, perm, hs));
+  SVG_TRY(launch_segsum(eb, H, N, d, C, perm, offsets, w.chunk_prefix, ntensors, src, dst,
+                        w.partial, hs));
+  bool any = false;
+  if (means)
+    for (int k = 0; k < ntensors; ++k) any = any || means[k];
+  if (any)
+    SVG_TRY(launch_combine(eb, H, d, C, ntensors, offsets, w.chunk_prefix, w.partial, N, means,
+                           /*mode=*/0, nullptr, nullptr, hs));
+  return SVGEAR_OK;
+}
+
+size_t svgear_probe_workspace(int H, int Nk, int Cq, int Ck) {
+  if (H < 1 || Nk < 1 || Cq < 1 || Ck < 1 || Ck > Nk || Ck > kMaxClusters || Cq > kMaxClusters)
+    return 0;
+  return probe_ws_bytes(H, Nk, Cq, Ck);
+}
+
+svgear_status svgear_probe(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck, float scale,
+                           const float* q_centroids, const void* Kp, const float* k_centroids,
+                           const int32_t* k_offsets, float* ratio, float* log_norm, void* ws,
+                           size_t ws_bytes, svgear_stream_t s) {
+  const svgear_status st = check_shape(dt, H, Nk, d, Ck);
+  if (st != SVGEAR_OK) return st;
+  if (Cq < 1 || Cq > kMaxClusters || !(scale > 0.f) || !q_centroids || !Kp || !k_centroids ||
+      !k_offsets || !ratio)
+    return SVGEAR_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < probe_ws_bytes(H, Nk, Cq, Ck)) return SVGEAR_ERR_WORKSPACE;
+  char* p = static_cast<char*>(ws);
+  int32_t* up = reinterpret_cast<int32_t*>(p);
+  float* rec = reinterpret_cast<float*>(p + align256(sizeof(int32_t) * size_t(H) * (Ck + 1)));
+  SVG_TRY(launch_probe(elem_bytes(dt), H, Nk, d, Cq, Ck, scale, q_centroids, Kp, k_centroids,
+                       k_offsets, up, rec, ratio, log_norm, as_stream(s)));
+  return SVGEAR_OK;
+}
+
+svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int32_t* k_offsets,
+                           int32_t budget_keys, uint8_t* sel_mask, int32_t* sel_list,
+                           int32_t* sel_count, int32_t* sel_keys, svgear_stream_t s) {
+  if (H < 1 || Cq < 1 || Ck < 1 || Cq > kMaxClusters || Ck > kMaxClusters || budget_keys < 0 ||
+      !ratio || !k_offsets || !sel_mask)
+    return SVGEAR_ERR_INVALID_ARG;
+  SVG_TRY(launch_route(H, Cq, Ck, ratio, k_offsets, budget_keys, sel_mask, sel_list, sel_count,
+                       sel_keys, as_stream(s)));
+  return SVGEAR_OK;
+}
+
+svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
+                            float scale, const void* Qp, const void* Kp, const void* Vp,
+                            const int32_t* q_offsets, const int32_t* k_offsets,
+                            const float* k_centroids, const float* v_centroids,
+                            const uint8_t* sel_mask, void* Op, svgear_stream_t s) {
+  svgear_status st = check_shape(dt, H, Nq, d, Cq);
+  if (st != SVGEAR_OK) return st;
+  st = check_shape(dt, H, Nk, d, Ck);
+  if (st != SVGEAR_OK) return st;
+  if (!(scale > 0.f) || !Qp || !Kp || !Vp || !q_offsets || !k_offsets || !k_centroids ||
+      !v_centroids || !sel_mask || !Op)
+    return SVGEAR_ERR_INVALID_ARG;
+  SVG_TRY(launch_attend(elem_bytes(dt), H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets,
+                        k_offsets, k_centroids, v_centroids, sel_mask, Op, as_stream(s)));
+  return SVGEAR_OK;
+}
+
+svgear_status svgear_unpermute(svgear_dtype dt, int H, int N, int d, const int32_t* perm,
+                               const void* Xp, void* X, svgear_stream_t s) {
+  const svgear_status st = check_shape(dt, H, N, d, 1);
+  if (st != SVGEAR_OK) return st;
+  if (!perm || !Xp || !X || Xp == X) return SVGEAR_ERR_INVALID_ARG;
+  SVG_TRY(launch_unpermute(elem_bytes(dt), H, N, d, perm, Xp, X, as_stream(s)));
+  return SVGEAR_OK;
+}
+
+}  // extern "C"

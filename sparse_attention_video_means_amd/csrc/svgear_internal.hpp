@@ -1,0 +1,81 @@
+// Host-side launchers shared between the svgear translation units. Not part
+// of the public ABI (include/svgear.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace svg {
+
+constexpr int kTile = 256;        // rows per counting-sort tile (one block)
+constexpr int kChunk = 1024;      // rows per segment-sum chunk
+constexpr int kProbeUnit = 256;   // keys per probe work unit
+constexpr int kProbeGroup = 128;  // query centroids per probe block
+constexpr int kMaxClusters = 1024;
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline int sort_tiles(int N) { return ceil_div(N, kTile); }
+inline int max_chunks(int N, int C) { return ceil_div(N, kChunk) + C; }
+inline int max_units(int Nk, int Ck) { return ceil_div(Nk, kProbeUnit) + Ck; }
+
+// Workspace carve-up for a counting sort + segment means over H heads.
+struct SortWs {
+  int32_t* rank;          // [H][N]
+  int32_t* hist;          // [H][C][tiles] -> exclusive bases after the scan
+  int32_t* chunk_prefix;  // [H][C+1]
+  float* partial;         // [H][ntensors][max_chunks][d]
+};
+size_t sort_ws_bytes(int H, int N, int d, int C, int ntensors);
+SortWs sort_ws_carve(void* ws, int H, int N, int d, int C, int ntensors);
+
+// sort.hip
+hipError_t launch_label_rank(const int32_t* labels, int H, int N, int C, int32_t* rank,
+                             int32_t* hist, hipStream_t s);
+hipError_t launch_sort_scan(int H, int N, int C, int32_t* hist, int32_t* offsets,
+                            int32_t* counts, int32_t* chunk_prefix, hipStream_t s);
+hipError_t launch_scatter(const int32_t* labels, const int32_t* rank, const int32_t* hist,
+                          int H, int N, int C, int32_t* perm, hipStream_t s);
+// Gathers rows of up to three tensors in permuted order (dst entries may be
+// null) and writes per-chunk f32 column sums to `partial`.
+hipError_t launch_segsum(int elem_bytes, int H, int N, int d, int C, const int32_t* perm,
+                         const int32_t* offsets, const int32_t* chunk_prefix, int ntensors,
+                         const void* const* src, void* const* dst, float* partial,
+                         hipStream_t s);
+// mode 0: empty cluster -> zero row; mode 1: empty cluster keeps `means`.
+// When `table` is non-null also writes table = -2 * round_T(mean) and
+// norms = ||round_T(mean)||^2 (k-means distance operands).
+hipError_t launch_combine(int elem_bytes, int H, int d, int C, int ntensors,
+                          const int32_t* offsets, const int32_t* chunk_prefix,
+                          const float* partial, int N, float* const* means, int mode,
+                          void* table, float* norms, hipStream_t s);
+hipError_t launch_unpermute(int elem_bytes, int H, int N, int d, const int32_t* perm,
+                            const void* Xp, void* X, hipStream_t s);
+
+// kmeans.hip
+hipError_t launch_table(int elem_bytes, int H, int d, int C, const float* mu, void* table,
+                        float* norms, hipStream_t s);
+hipError_t launch_assign(int elem_bytes, int H, int N, int d, int C, const void* X,
+                         const void* table, const float* norms, int32_t* labels, int32_t* rank,
+                         int32_t* hist, hipStream_t s);
+
+// probe.hip
+hipError_t launch_probe(int elem_bytes, int H, int Nk, int d, int Cq, int Ck, float scale,
+                        const float* qc, const void* Kp, const float* kc, const int32_t* koff,
+                        int32_t* unit_prefix, float* rec, float* ratio, float* log_norm,
+                        hipStream_t s);
+
+// route.hip
+hipError_t launch_route(int H, int Cq, int Ck, const float* ratio, const int32_t* koff,
+                        int32_t budget, uint8_t* mask, int32_t* list, int32_t* count,
+                        int32_t* keys, hipStream_t s);
+
+// attend.hip
+hipError_t launch_attend(int elem_bytes, int H, int Nq, int Nk, int d, int Cq, int Ck,
+                         float scale, const void* Qp, const void* Kp, const void* Vp,
+                         const int32_t* qoff, const int32_t* koff, const float* kc,
+                         const float* vc, const uint8_t* mask, void* Op, hipStream_t s);
+
+}  // namespace svg

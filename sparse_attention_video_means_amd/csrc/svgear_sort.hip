@@ -1,0 +1,313 @@
+// Deterministic counting sort of cluster labels, gathered copies and segment
+// means (the permutation and centroid stages of SVG-EAR, paper §3.1 / §4.1:
+// tokens of a cluster are laid out contiguously and summarised by their mean).
+//
+// Pipeline for one tensor family, all heads at once:
+//   label_rank  : per 256-row tile, stable rank of each row among equal labels
+//                 of the tile (wave ballots, no atomics) + tile histogram.
+//   sort_scan   : per head, exclusive scan of the [cluster][tile] histogram in
+//                 cluster-major order -> every tile's base slot per cluster,
+//                 cluster offsets and the per-cluster chunk list.
+//   scatter     : perm[base + rank] = row (stable by construction).
+//   segsum      : per chunk of <= 1024 slots of one cluster, gather the rows
+//                 (optionally storing the permuted copy) and sum them in f32 in a
+//                 fixed order.
+//   combine     : per cluster, add its chunk sums in chunk order and divide.
+// Every step has a fixed reduction order, so results are bitwise repeatable.
+#include "svgear_common.hpp"
+#include "svgear_internal.hpp"
+
+namespace svg {
+
+size_t sort_ws_bytes(int H, int N, int d, int C, int ntensors) {
+  size_t b = 0;
+  b += align256(sizeof(int32_t) * size_t(H) * N);
+  b += align256(sizeof(int32_t) * size_t(H) * C * sort_tiles(N));
+  b += align256(sizeof(int32_t) * size_t(H) * (C + 1));
+  b += align256(sizeof(float) * size_t(H) * ntensors * max_chunks(N, C) * d);
+  return b;
+}
+
+SortWs sort_ws_carve(void* ws, int H, int N, int d, int C, int ntensors) {
+  char* p = static_cast<char*>(ws);
+  SortWs w;
+  w.rank = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * size_t(H) * N);
+  w.hist = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * size_t(H) * C * sort_tiles(N));
+  w.chunk_prefix = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * size_t(H) * (C + 1));
+  w.partial = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void label_rank_kernel(const int32_t* __restrict__ labels,
+                                                         int N, int C, int tiles,
+                                                         int32_t* __restrict__ rank,
+                                                         int32_t* __restrict__ hist) {
+  extern __shared__ int wave_hist[];
+  const int h = blockIdx.y, t = blockIdx.x, tid = threadIdx.x;
+  const int n = t * kTile + tid;
+  const bool valid = n < N;
+  // labels outside [0, C) are clamped so that no access leaves its buffer
+  const int label = valid ? min(max(labels[size_t(h) * N + n], 0), C - 1) : 0;
+  const int r = tile_rank(label, valid, C, wave_hist);
+  if (valid) rank[size_t(h) * N + n] = r;
+  for (int c = tid; c < C; c += 256)
+    hist[(size_t(h) * C + c) * tiles + t] =
+        wave_hist[c] + wave_hist[C + c] + wave_hist[2 * C + c] + wave_hist[3 * C + c];
+}
+
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int N, int C, int tiles,
+                                                         int32_t* __restrict__ hist,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ chunk_prefix) {
+  __shared__ int scratch[16];
+  __shared__ int off_s[kMaxClusters + 1];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const size_t E = size_t(C) * tiles;
+  int32_t* base = hist + size_t(h) * E;
+  int carry = 0;
+  for (size_t r0 = 0; r0 < E; r0 += 1024) {
+    const size_t idx = r0 + tid;
+    const int v = idx < E ? base[idx] : 0;
+    int tot;
+    const int ex = block_exclusive_scan(v, scratch, &tot);
+    if (idx < E) {
+      base[idx] = carry + ex;
+      if (idx % tiles == 0) off_s[idx / tiles] = carry + ex;
+    }
+    carry += tot;
+  }
+  if (tid == 0) off_s[C] = carry;
+  __syncthreads();
+  int chunks = 0;
+  if (tid < C) {
+    const int cnt = off_s[tid + 1] - off_s[tid];
+    offsets[size_t(h) * (C + 1) + tid] = off_s[tid];
+    if (counts) counts[size_t(h) * C + tid] = cnt;
+    chunks = (cnt + kChunk - 1) / kChunk;
+  }
+  if (tid == 0) offsets[size_t(h) * (C + 1) + C] = off_s[C];
+  int total;
+  const int ex = block_exclusive_scan(chunks, scratch, &total);
+  if (tid < C) chunk_prefix[size_t(h) * (C + 1) + tid] = ex;
+  if (tid == 0) chunk_prefix[size_t(h) * (C + 1) + C] = total;
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ labels,
+                                                      const int32_t* __restrict__ rank,
+                                                      const int32_t* __restrict__ base, int N,
+                                                      int C, int tiles,
+                                                      int32_t* __restrict__ perm) {
+  const int h = blockIdx.y, t = blockIdx.x;
+  const int n = t * kTile + threadIdx.x;
+  if (n >= N) return;
+  const int lab = min(max(labels[size_t(h) * N + n], 0), C - 1);
+  const int p = base[(size_t(h) * C + lab) * tiles + t] + rank[size_t(h) * N + n];
+  perm[size_t(h) * N + p] = n;
+}
+
+// Cluster c owning chunk q: the largest c with chunk_prefix[c] <= q.
+__device__ __forceinline__ int find_segment(const int32_t* prefix, int C, int q) {
+  int lo = 0, hi = C;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= q) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+struct Ptr3 {
+  const void* p[3];
+};
+struct MutPtr3 {
+  void* p[3];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void segsum_kernel(int N, int C, int nt, int maxch,
+                                                     const int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ chunk_prefix,
+                                                     Ptr3 src, MutPtr3 dst,
+                                                     float* __restrict__ partial) {
+  constexpr int EPT = 16 / sizeof(T);       // elements per 16-byte access
+  constexpr int TPR = D / EPT;              // threads per row
+  constexpr int RPI = 256 / TPR;            // rows per iteration
+  __shared__ float red[RPI][D];
+  const int h = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
+  const int32_t* cp = chunk_prefix + size_t(h) * (C + 1);
+  if (q >= cp[C]) return;
+  const int c = find_segment(cp, C, q);
+  const int32_t* off = offsets + size_t(h) * (C + 1);
+  const int p0 = off[c] + (q - cp[c]) * kChunk;
+  const int p1 = min(off[c + 1], p0 + kChunk);
+  const int rg = tid / TPR, col = tid % TPR;
+  for (int k = 0; k < nt; ++k) {
+    const T* s = static_cast<const T*>(src.p[k]) + size_t(h) * N * D;
+    T* dd = dst.p[k] ? static_cast<T*>(dst.p[k]) + size_t(h) * N * D : nullptr;
+    float acc[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+    for (int p = p0 + rg; p < p1; p += RPI) {
+      const int row = perm[size_t(h) * N + p];
+      uint4 v = *reinterpret_cast<const uint4*>(s + size_t(row) * D + col * EPT);
+      if (dd) *reinterpret_cast<uint4*>(dd + size_t(p) * D + col * EPT) = v;
+      const T* el = reinterpret_cast<const T*>(&v);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) acc[e] += to_f32(el[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) red[rg][col * EPT + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+      float sum = 0.f;
+      for (int r = 0; r < RPI; ++r) sum += red[r][tid];
+      partial[((size_t(h) * nt + k) * maxch + q) * D + tid] = sum;
+    }
+    __syncthreads();
+  }
+}
+
+struct FPtr3 {
+  float* p[3];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void combine_kernel(int C, int nt, int maxch,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ chunk_prefix,
+                                                    const float* __restrict__ partial, FPtr3 means,
+                                                    int mode, T* __restrict__ table,
+                                                    float* __restrict__ norms) {
+  __shared__ float wsum[2];
+  const int h = blockIdx.y, c = blockIdx.x, j = threadIdx.x;
+  const int32_t* off = offsets + size_t(h) * (C + 1);
+  const int32_t* cp = chunk_prefix + size_t(h) * (C + 1);
+  const int n = off[c + 1] - off[c];
+  for (int k = 0; k < nt; ++k) {
+    float* mk = means.p[k];
+    float m;
+    if (n > 0) {
+      float s = 0.f;
+      for (int q = cp[c]; q < cp[c + 1]; ++q) s += partial[((size_t(h) * nt + k) * maxch + q) * D + j];
+      m = s / float(n);
+    } else {
+      m = (mode == 0 || !mk) ? 0.f : mk[(size_t(h) * C + c) * D + j];
+    }
+    if (mk) mk[(size_t(h) * C + c) * D + j] = m;
+    if (k == 0 && table) {
+      const T r = from_f32<T>(m);
+      const float rf = to_f32(r);
+      table[(size_t(h) * C + c) * D + j] = from_f32<T>(-2.f * rf);
+      float sq = rf * rf;
+      for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+      if ((j & 63) == 0) wsum[j >> 6] = sq;
+      __syncthreads();
+      if (j == 0) norms[size_t(h) * C + c] = (D > 64) ? wsum[0] + wsum[1] : wsum[0];
+      __syncthreads();
+    }
+  }
+}
+
+__global__ void unpermute_kernel(int N, int cpr, const int32_t* __restrict__ perm,
+                                 const uint4* __restrict__ Xp, uint4* __restrict__ X) {
+  const int h = blockIdx.y;
+  const size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= size_t(N) * cpr) return;
+  const int p = int(idx / cpr), k = int(idx % cpr);
+  const int row = perm[size_t(h) * N + p];
+  X[(size_t(h) * N + row) * cpr + k] = Xp[(size_t(h) * N + p) * cpr + k];
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_label_rank(const int32_t* labels, int H, int N, int C, int32_t* rank,
+                             int32_t* hist, hipStream_t s) {
+  const int tiles = sort_tiles(N);
+  hipLaunchKernelGGL(label_rank_kernel, dim3(tiles, H), dim3(256), 4 * C * sizeof(int), s, labels,
+                     N, C, tiles, rank, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_scan(int H, int N, int C, int32_t* hist, int32_t* offsets,
+                            int32_t* counts, int32_t* chunk_prefix, hipStream_t s) {
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(H), dim3(1024), 0, s, N, C, sort_tiles(N), hist,
+                     offsets, counts, chunk_prefix);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const int32_t* labels, const int32_t* rank, const int32_t* hist,
+                          int H, int N, int C, int32_t* perm, hipStream_t s) {
+  const int tiles = sort_tiles(N);
+  hipLaunchKernelGGL(scatter_kernel, dim3(tiles, H), dim3(256), 0, s, labels, rank, hist, N, C,
+                     tiles, perm);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static void segsum_t(int H, int N, int C, const int32_t* perm, const int32_t* offsets,
+                     const int32_t* cp, int nt, const void* const* src, void* const* dst,
+                     float* partial, hipStream_t s) {
+  Ptr3 sp{};
+  MutPtr3 dp{};
+  for (int k = 0; k < nt; ++k) {
+    sp.p[k] = src[k];
+    dp.p[k] = dst ? dst[k] : nullptr;
+  }
+  const int maxch = max_chunks(N, C);
+  hipLaunchKernelGGL((segsum_kernel<T, D>), dim3(maxch, H), dim3(256), 0, s, N, C, nt, maxch,
+                     perm, offsets, cp, sp, dp, partial);
+}
+
+hipError_t launch_segsum(int elem_bytes, int H, int N, int d, int C, const int32_t* perm,
+                         const int32_t* offsets, const int32_t* chunk_prefix, int ntensors,
+                         const void* const* src, void* const* dst, float* partial,
+                         hipStream_t s) {
+  if (elem_bytes == 2) {
+    if (d == 128) segsum_t<__bf16, 128>(H, N, C, perm, offsets, chunk_prefix, ntensors, src, dst, partial, s);
+    else segsum_t<__bf16, 64>(H, N, C, perm, offsets, chunk_prefix, ntensors, src, dst, partial, s);
+  } else {
+    if (d == 128) segsum_t<float, 128>(H, N, C, perm, offsets, chunk_prefix, ntensors, src, dst, partial, s);
+    else segsum_t<float, 64>(H, N, C, perm, offsets, chunk_prefix, ntensors, src, dst, partial, s);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static void combine_t(int H, int C, int nt, const int32_t* offsets, const int32_t* cp,
+                      const float* partial, int N, float* const* means, int mode, void* table,
+                      float* norms, hipStream_t s) {
+  FPtr3 mp{};
+  for (int k = 0; k < nt; ++k) mp.p[k] = means ? means[k] : nullptr;
+  hipLaunchKernelGGL((combine_kernel<T, D>), dim3(C, H), dim3(D), 0, s, C, nt, max_chunks(N, C),
+                     offsets, cp, partial, mp, mode, static_cast<T*>(table), norms);
+}
+
+hipError_t launch_combine(int elem_bytes, int H, int d, int C, int ntensors,
+                          const int32_t* offsets, const int32_t* chunk_prefix,
+                          const float* partial, int N, float* const* means, int mode,
+                          void* table, float* norms, hipStream_t s) {
+  if (elem_bytes == 2) {
+    if (d == 128) combine_t<__bf16, 128>(H, C, ntensors, offsets, chunk_prefix, partial, N, means, mode, table, norms, s);
+    else combine_t<__bf16, 64>(H, C, ntensors, offsets, chunk_prefix, partial, N, means, mode, table, norms, s);
+  } else {
+    if (d == 128) combine_t<float, 128>(H, C, ntensors, offsets, chunk_prefix, partial, N, means, mode, table, norms, s);
+    else combine_t<float, 64>(H, C, ntensors, offsets, chunk_prefix, partial, N, means, mode, table, norms, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(int elem_bytes, int H, int N, int d, const int32_t* perm,
+                            const void* Xp, void* X, hipStream_t s) {
+  const int cpr = d * elem_bytes / 16;
+  const size_t total = size_t(N) * cpr;
+  const int blocks = int((total + 255) / 256);
+  hipLaunchKernelGGL(unpermute_kernel, dim3(blocks, H), dim3(256), 0, s, N, cpr, perm,
+                     static_cast<const uint4*>(Xp), static_cast<uint4*>(X));
+  return hipGetLastError();
+}
+
+}  // namespace svg

@@ -1,0 +1,92 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function include/svgear.h declares, and
+reject bad arguments synchronously with the documented status codes before
+it touches the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svgear.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_attention_video_means_amd import svgear
+    if not os.path.exists(svgear.LIB_PATH):
+        from sparse_attention_video_means_amd import build
+        build.build()
+    return svgear.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svgear_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_six_calls():
+    names = declared_functions()
+    for call in ("cluster", "permute", "probe", "route", "attend", "unpermute"):
+        assert f"svgear_{call}" in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from sparse_attention_video_means_amd import svgear
+    names = declared_functions()
+    assert set(names) == set(svgear.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.svgear_status_string(0) == b"ok"
+    assert L.svgear_status_string(3) == b"workspace too small"
+    assert L.svgear_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries(L):
+    a = L.svgear_cluster_workspace(1, 40, 75600, 128, 500)
+    b = L.svgear_cluster_workspace(1, 40, 75600, 128, 100)
+    assert a > b > 0
+    assert L.svgear_cluster_workspace(1, 1, 10, 128, 11) == 0      # C > N
+    assert L.svgear_cluster_workspace(1, 1, 2000, 96, 10) == 0     # d not built
+    assert L.svgear_cluster_workspace(1, 1, 5000, 128, 1025) == 0  # C > 1024
+    assert L.svgear_permute_workspace(1, 8, 16384, 128, 500) > 0
+    assert L.svgear_probe_workspace(40, 75600, 100, 500) > 0
+    assert L.svgear_probe_workspace(1, 100, 10, 200) == 0          # Ck > Nk
+
+
+def test_argument_errors_return_before_any_launch(L):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    null = None
+    # null input
+    assert L.svgear_cluster(1, 1, 100, 64, 4, 1, null, fake, fake, fake, fake, 1 << 30, null) == 1
+    # iters < 1
+    assert L.svgear_cluster(1, 1, 100, 64, 4, 0, fake, fake, fake, fake, fake, 1 << 30, null) == 1
+    # unsupported head dim / dtype
+    assert L.svgear_cluster(1, 1, 100, 80, 4, 1, fake, fake, fake, fake, fake, 1 << 30, null) == 2
+    assert L.svgear_cluster(7, 1, 100, 64, 4, 1, fake, fake, fake, fake, fake, 1 << 30, null) == 2
+    # workspace too small
+    assert L.svgear_cluster(1, 1, 100, 64, 4, 1, fake, fake, fake, fake, fake, 16, null) == 3
+    # permute: src aliases dst
+    arr = (ctypes.c_void_p * 1)(0x1000)
+    assert L.svgear_permute(1, 1, 100, 64, 4, fake, fake, fake, 1, arr, arr, None, fake,
+                            1 << 30, null) == 1
+    assert L.svgear_permute(1, 1, 100, 64, 4, fake, fake, fake, 3, arr, arr, None, fake,
+                            1 << 30, null) == 1
+    # probe: scale must be positive
+    assert L.svgear_probe(1, 1, 100, 64, 4, 4, 0.0, fake, fake, fake, fake, fake, null, fake,
+                          1 << 30, null) == 1
+    # route: negative budget, Ck too large
+    assert L.svgear_route(1, 4, 4, fake, fake, -1, fake, null, null, null, null) == 1
+    assert L.svgear_route(1, 4, 2000, fake, fake, 5, fake, null, null, null, null) == 1
+    # attend: C > N on the key side
+    assert L.svgear_attend(1, 1, 100, 10, 64, 4, 11, 0.1, fake, fake, fake, fake, fake, fake,
+                           fake, fake, fake, null) == 1
+    # unpermute: aliasing
+    assert L.svgear_unpermute(1, 1, 100, 64, fake, fake, fake, null) == 1
