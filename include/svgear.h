@@ -171,13 +171,18 @@ svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int3
  *
  *   Qp [H][Nq][d], Kp/Vp [H][Nk][d] dt;  q_offsets [H][Cq+1], k_offsets [H][Ck+1];
  *   k_centroids, v_centroids [H][Ck][d] f32;  sel_mask [H][Cq][Ck] uint8;
- *   Op [H][Nq][d] dt out (rows in the permuted query order).
+ *   Op [H][Nq][d] dt out (rows in the permuted query order);
+ *   ws  workspace of svgear_attend_workspace(...) bytes (it holds the centroid
+ *       rows rounded to dt); may be NULL when that size is 0.
  */
+size_t svgear_attend_workspace(svgear_dtype dt, int H, int Ck, int d);
+
 svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
                             float scale, const void* Qp, const void* Kp, const void* Vp,
                             const int32_t* q_offsets, const int32_t* k_offsets,
                             const float* k_centroids, const float* v_centroids,
-                            const uint8_t* sel_mask, void* Op, svgear_stream_t s);
+                            const uint8_t* sel_mask, void* Op, void* ws, size_t ws_bytes,
+                            svgear_stream_t s);
 
 /*
  * Inverse permutation of output rows: X[h][perm[h][p]] = Xp[h][p] (paper §3.1).

@@ -21,6 +21,9 @@ ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: the kernels fit in 256 VGPRs and the
+    # AGPR form makes the register allocator copy accumulators every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -178,11 +178,17 @@ svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int3
   return SVGEAR_OK;
 }
 
+size_t svgear_attend_workspace(svgear_dtype dt, int H, int Ck, int d) {
+  if (H < 1 || Ck < 1 || Ck > kMaxClusters || elem_bytes(dt) == 0 || !dim_ok(d)) return 0;
+  return attend_ws_bytes(elem_bytes(dt), H, Ck, d);
+}
+
 svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
                             float scale, const void* Qp, const void* Kp, const void* Vp,
                             const int32_t* q_offsets, const int32_t* k_offsets,
                             const float* k_centroids, const float* v_centroids,
-                            const uint8_t* sel_mask, void* Op, svgear_stream_t s) {
+                            const uint8_t* sel_mask, void* Op, void* ws, size_t ws_bytes,
+                            svgear_stream_t s) {
   svgear_status st = check_shape(dt, H, Nq, d, Cq);
   if (st != SVGEAR_OK) return st;
   st = check_shape(dt, H, Nk, d, Ck);
@@ -190,8 +196,10 @@ svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int C
   if (!(scale > 0.f) || !Qp || !Kp || !Vp || !q_offsets || !k_offsets || !k_centroids ||
       !v_centroids || !sel_mask || !Op)
     return SVGEAR_ERR_INVALID_ARG;
+  const size_t need = attend_ws_bytes(elem_bytes(dt), H, Ck, d);
+  if (need > 0 && (!ws || ws_bytes < need)) return SVGEAR_ERR_WORKSPACE;
   SVG_TRY(launch_attend(elem_bytes(dt), H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets,
-                        k_offsets, k_centroids, v_centroids, sel_mask, Op, as_stream(s)));
+                        k_offsets, k_centroids, v_centroids, sel_mask, Op, ws, as_stream(s)));
   return SVGEAR_OK;
 }
 

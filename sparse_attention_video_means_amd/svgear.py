@@ -52,8 +52,9 @@ def lib() -> ctypes.CDLL:
             "svgear_probe": (i32, [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
                                    sz, vp]),
             "svgear_route": (i32, [i32, i32, i32, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]),
+            "svgear_attend_workspace": (sz, [i32, i32, i32, i32]),
             "svgear_attend": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
-                                    vp, vp, vp, vp]),
+                                    vp, vp, vp, vp, sz, vp]),
             "svgear_unpermute": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
@@ -66,7 +67,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
            "svgear_permute_workspace", "svgear_permute", "svgear_probe_workspace", "svgear_probe",
-           "svgear_route", "svgear_attend", "svgear_unpermute")
+           "svgear_route", "svgear_attend_workspace", "svgear_attend", "svgear_unpermute")
 
 
 def _check(fn: str, code: int):
@@ -207,11 +208,13 @@ def svgear_attend(qp, kp, vp, q_offsets, k_offsets, k_centroids, v_centroids, se
     _need(sel_mask, "sel_mask", torch.uint8, (H, Cq, Ck))
     op = torch.empty_like(qp) if out is None else out
     _need(op, "out", qp.dtype, qp.shape)
-    _check("svgear_attend", lib().svgear_attend(_dt(qp), H, Nq, Nk, d, Cq, Ck, float(scale),
-                                                _ptr(qp), _ptr(kp), _ptr(vp), _ptr(q_offsets),
-                                                _ptr(k_offsets), _ptr(k_centroids),
-                                                _ptr(v_centroids), _ptr(sel_mask), _ptr(op),
-                                                _stream()))
+    L = lib()
+    ws = _ws(L.svgear_attend_workspace(_dt(qp), H, Ck, d), qp.device)
+    _check("svgear_attend", L.svgear_attend(_dt(qp), H, Nq, Nk, d, Cq, Ck, float(scale),
+                                            _ptr(qp), _ptr(kp), _ptr(vp), _ptr(q_offsets),
+                                            _ptr(k_offsets), _ptr(k_centroids),
+                                            _ptr(v_centroids), _ptr(sel_mask), _ptr(op),
+                                            _ptr(ws), ws.numel(), _stream()))
     return op
 
 
@@ -265,7 +268,8 @@ class RoutedAttention:
                   L.svgear_cluster_workspace(self.dt, H, nk, d, ck),
                   L.svgear_permute_workspace(self.dt, H, nq, d, cq),
                   L.svgear_permute_workspace(self.dt, H, nk, d, ck),
-                  L.svgear_probe_workspace(H, nk, cq, ck))
+                  L.svgear_probe_workspace(H, nk, cq, ck),
+                  L.svgear_attend_workspace(self.dt, H, ck, d))
         self.ws = _ws(wsz, device)
         self._events = None
 
@@ -311,7 +315,7 @@ class RoutedAttention:
                                                 _ptr(self.qp), _ptr(self.kp), _ptr(self.vp),
                                                 _ptr(self.q_off), _ptr(self.k_off),
                                                 _ptr(self.k_bar), _ptr(self.v_bar),
-                                                _ptr(self.sel_mask), _ptr(self.op), s))
+                                                _ptr(self.sel_mask), _ptr(self.op), ws, wn, s))
         mark(13); mark(14)
         _check("svgear_unpermute", L.svgear_unpermute(dt, H, nq, d, _ptr(self.perm_q),
                                                       _ptr(self.op), _ptr(self.o), s))

@@ -87,6 +87,11 @@ def test_argument_errors_return_before_any_launch(L):
     assert L.svgear_route(1, 4, 2000, fake, fake, 5, fake, null, null, null, null) == 1
     # attend: C > N on the key side
     assert L.svgear_attend(1, 1, 100, 10, 64, 4, 11, 0.1, fake, fake, fake, fake, fake, fake,
-                           fake, fake, fake, null) == 1
+                           fake, fake, fake, fake, 1 << 30, null) == 1
+    # attend: bf16 needs a workspace for the rounded centroid rows
+    assert L.svgear_attend_workspace(1, 2, 50, 128) > 0
+    assert L.svgear_attend_workspace(0, 2, 50, 128) == 0
+    assert L.svgear_attend(1, 1, 100, 100, 64, 4, 11, 0.1, fake, fake, fake, fake, fake, fake,
+                           fake, fake, fake, null, 0, null) == 3
     # unpermute: aliasing
     assert L.svgear_unpermute(1, 1, 100, 64, fake, fake, fake, null) == 1
