@@ -54,10 +54,6 @@ ClusterWs cluster_ws_carve(void* ws, int eb, int H, int N, int d, int C) {
   return w;
 }
 
-size_t probe_ws_bytes(int H, int Nk, int Cq, int Ck) {
-  return align256(sizeof(int32_t) * size_t(H) * (Ck + 1)) +
-         align256(sizeof(float) * 3 * size_t(H) * max_units(Nk, Ck) * Cq);
-}
 
 #define SVG_TRY(expr)                                      \
   do {                                                     \
@@ -97,8 +93,9 @@ svgear_status svgear_cluster(svgear_dtype dt, int H, int N, int d, int C, int it
   SVG_TRY(launch_table(eb, H, d, C, centroids, w.table, w.norms, hs));
   for (int it = 0; it < iters; ++it) {
     SVG_TRY(launch_assign(eb, H, N, d, C, X, w.table, w.norms, labels, w.sort.rank, w.sort.hist, hs));
-    SVG_TRY(launch_sort_scan(H, N, C, w.sort.hist, w.offsets, counts, w.sort.chunk_prefix, hs));
-    SVG_TRY(launch_scatter(labels, w.sort.rank, w.sort.hist, H, N, C, w.perm, hs));
+    SVG_TRY(launch_sort_scan(H, N, C, w.sort.hist, w.sort.sizes, w.offsets, counts,
+                             w.sort.chunk_prefix, hs));
+    SVG_TRY(launch_scatter(labels, w.sort.rank, w.sort.hist, w.offsets, H, N, C, w.perm, hs));
     const void* src[1] = {X};
     SVG_TRY(launch_segsum(eb, H, N, d, C, w.perm, w.offsets, w.sort.chunk_prefix, 1, src, nullptr,
                           w.sort.partial, hs));
@@ -130,8 +127,8 @@ svgear_status svgear_permute(svgear_dtype dt, int H, int N, int d, int C, const 
   const hipStream_t hs = as_stream(s);
   SortWs w = sort_ws_carve(ws, H, N, d, C, 2);
   SVG_TRY(launch_label_rank(labels, H, N, C, w.rank, w.hist, hs));
-  SVG_TRY(launch_sort_scan(H, N, C, w.hist, offsets, nullptr, w.chunk_prefix, hs));
-  SVG_TRY(launch_scatter(labels, w.rank, w.hist, H, N, C, perm, hs));
+  SVG_TRY(launch_sort_scan(H, N, C, w.hist, w.sizes, offsets, nullptr, w.chunk_prefix, hs));
+  SVG_TRY(launch_scatter(labels, w.rank, w.hist, offsets, H, N, C, perm, hs));
   SVG_TRY(launch_segsum(eb, H, N, d, C, perm, offsets, w.chunk_prefix, ntensors, src, dst,
                         w.partial, hs));
   bool any = false;
@@ -159,11 +156,8 @@ svgear_status svgear_probe(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck
       !k_offsets || !ratio)
     return SVGEAR_ERR_INVALID_ARG;
   if (!ws || ws_bytes < probe_ws_bytes(H, Nk, Cq, Ck)) return SVGEAR_ERR_WORKSPACE;
-  char* p = static_cast<char*>(ws);
-  int32_t* up = reinterpret_cast<int32_t*>(p);
-  float* rec = reinterpret_cast<float*>(p + align256(sizeof(int32_t) * size_t(H) * (Ck + 1)));
   SVG_TRY(launch_probe(elem_bytes(dt), H, Nk, d, Cq, Ck, scale, q_centroids, Kp, k_centroids,
-                       k_offsets, up, rec, ratio, log_norm, as_stream(s)));
+                       k_offsets, ws, ratio, log_norm, as_stream(s)));
   return SVGEAR_OK;
 }
 

@@ -26,6 +26,7 @@ struct SortWs {
   int32_t* rank;          // [H][N]
   int32_t* hist;          // [H][C][tiles] -> exclusive bases after the scan
   int32_t* chunk_prefix;  // [H][C+1]
+  int32_t* sizes;         // [H][C]
   float* partial;         // [H][ntensors][max_chunks][d]
 };
 size_t sort_ws_bytes(int H, int N, int d, int C, int ntensors);
@@ -34,10 +35,12 @@ SortWs sort_ws_carve(void* ws, int H, int N, int d, int C, int ntensors);
 // sort.hip
 hipError_t launch_label_rank(const int32_t* labels, int H, int N, int C, int32_t* rank,
                              int32_t* hist, hipStream_t s);
-hipError_t launch_sort_scan(int H, int N, int C, int32_t* hist, int32_t* offsets,
+// hist [H][C][tiles] becomes every tile's exclusive prefix within its cluster.
+hipError_t launch_sort_scan(int H, int N, int C, int32_t* hist, int32_t* sizes, int32_t* offsets,
                             int32_t* counts, int32_t* chunk_prefix, hipStream_t s);
 hipError_t launch_scatter(const int32_t* labels, const int32_t* rank, const int32_t* hist,
-                          int H, int N, int C, int32_t* perm, hipStream_t s);
+                          const int32_t* offsets, int H, int N, int C, int32_t* perm,
+                          hipStream_t s);
 // Gathers rows of up to three tensors in permuted order (dst entries may be
 // null) and writes per-chunk f32 column sums to `partial`.
 hipError_t launch_segsum(int elem_bytes, int H, int N, int d, int C, const int32_t* perm,
@@ -62,10 +65,10 @@ hipError_t launch_assign(int elem_bytes, int H, int N, int d, int C, const void*
                          int32_t* hist, hipStream_t s);
 
 // probe.hip
+size_t probe_ws_bytes(int H, int Nk, int Cq, int Ck);
 hipError_t launch_probe(int elem_bytes, int H, int Nk, int d, int Cq, int Ck, float scale,
                         const float* qc, const void* Kp, const float* kc, const int32_t* koff,
-                        int32_t* unit_prefix, float* rec, float* ratio, float* log_norm,
-                        hipStream_t s);
+                        void* ws, float* ratio, float* log_norm, hipStream_t s);
 
 // route.hip
 hipError_t launch_route(int H, int Cq, int Ck, const float* ratio, const int32_t* koff,

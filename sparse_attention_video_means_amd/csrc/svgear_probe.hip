@@ -1,19 +1,23 @@
 // Query-centroid error probe (paper §4.2, Eq. 5; streaming kernel of §4.4).
 //
-// Work is split into units of at most 256 consecutive permuted keys that all
-// belong to ONE key cluster c'. A block takes one unit and up to 128 query
-// centroids (32 per wavefront). Keys are staged through LDS in 64-row tiles
-// and multiplied against the centroids on matrix cores (S^T = K qbar^T); the
-// f32 centroids enter as a bf16 high part plus a bf16 remainder, so the logits
-// carry about 16 significant bits. Because the unit lies inside one cluster,
-// the centroid logit s~ is the same for every key of the unit, and each lane
-// keeps a streaming triple relative to a running maximum m (initialised to s~):
-//     Z = sum exp(s - m),   E = sum (exp(s - m) - exp(s~ - m))^2.
-// The squared gap is accumulated directly rather than expanded, so tight
-// blocks (s ~ s~) do not lose their small error to cancellation. A finalize
-// pass rescales the unit triples of each query centroid to the global maximum
-// and forms ratio = E / (Z^2 |k_c'|). All exponentials are base 2 with log2(e)
-// folded into the scale. No atomics: results are bitwise repeatable.
+// For query centroid c and key j of key cluster c' the raw logit is
+// s = s~ + delta with s~ = scale*qbar_c.kbar_c' (the centroid logit, the same for
+// the whole block) and delta = scale*qbar_c.(k_j - kbar_c'). The kernels use
+// exactly this split:
+//   * centroid_logits: s~ for every (c, c') in f32 (a small Cq x Ck x d product);
+//   * probe: keys are staged through LDS as (k_j - kbar_c') rounded to the element
+//     type, and delta comes from the matrix cores against qbar_c. Because the
+//     differences are small, their rounding error is small in absolute terms,
+//     so tight blocks (delta ~ 0) keep an accurate error; the centroid side is
+//     split into a bf16 high part and a bf16 remainder (two products).
+// Work is split into units of at most 256 consecutive permuted keys of ONE key
+// cluster; persistent blocks walk the units of a head, keeping their 128 query
+// centroids as MFMA B operands in registers. Each lane keeps a streaming triple
+// relative to a running reference m >= s~ (base-2 logits):
+//     Z = sum exp2(s - m),   E = sum (exp2(s - m) - exp2(s~ - m))^2,
+// accumulated directly (the squared gap is never expanded). A finalize pass
+// rescales the unit triples of each query centroid to the global maximum and
+// forms ratio = E / (Z^2 |k_c'|). No atomics: results are bitwise repeatable.
 #include "svgear_common.hpp"
 #include "svgear_internal.hpp"
 
@@ -32,6 +36,28 @@ __global__ __launch_bounds__(1024) void probe_units_kernel(int Ck, const int32_t
   if (tid == 0) unit_prefix[size_t(h) * (Ck + 1) + Ck] = total;
 }
 
+// st2[h][c][c'] = sl2 * qbar_c . kbar_c'  (16 x 16 pairs per block, rows from LDS)
+template <int D>
+__global__ __launch_bounds__(256) void centroid_logits_kernel(int Cq, int Ck, float sl2,
+                                                              const float* __restrict__ qc,
+                                                              const float* __restrict__ kc,
+                                                              float* __restrict__ st2) {
+  __shared__ float qs[16][D + 1];
+  __shared__ float kcs[16][D + 1];
+  const int h = blockIdx.z, c0 = blockIdx.y * 16, k0 = blockIdx.x * 16, tid = threadIdx.x;
+  for (int i = tid; i < 16 * D; i += 256) {
+    const int r = i / D, j = i % D;
+    qs[r][j] = (c0 + r < Cq) ? qc[(size_t(h) * Cq + c0 + r) * D + j] : 0.f;
+    kcs[r][j] = (k0 + r < Ck) ? kc[(size_t(h) * Ck + k0 + r) * D + j] : 0.f;
+  }
+  __syncthreads();
+  const int a = tid / 16, b = tid % 16;
+  float dot = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < D; ++j) dot = fmaf(qs[a][j], kcs[b][j], dot);
+  if (c0 + a < Cq && k0 + b < Ck) st2[(size_t(h) * Cq + c0 + a) * Ck + k0 + b] = dot * sl2;
+}
+
 __device__ __forceinline__ int find_unit_cluster(const int32_t* prefix, int C, int q) {
   int lo = 0, hi = C;
   while (hi - lo > 1) {
@@ -41,155 +67,169 @@ __device__ __forceinline__ int find_unit_cluster(const int32_t* prefix, int C, i
   return lo;
 }
 
-template <typename T>
-__device__ __forceinline__ void split_centroid(const float (&x)[8], Frag<T>& hi, Frag<T>& lo,
-                                               float (&val)[8]);
-
-template <>
-__device__ __forceinline__ void split_centroid<__bf16>(const float (&x)[8], Frag<__bf16>& hi,
-                                                       Frag<__bf16>& lo, float (&val)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 a = __bf16(x[e]);
-    const __bf16 b = __bf16(x[e] - float(a));
-    hi.v[e] = a;
-    lo.v[e] = b;
-    val[e] = float(a) + float(b);
-  }
-}
-
-template <>
-__device__ __forceinline__ void split_centroid<float>(const float (&x)[8], Frag<float>& hi,
-                                                      Frag<float>& lo, float (&val)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    hi.v[e] = x[e];
-    lo.v[e] = 0.f;
-    val[e] = x[e];
-  }
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc,
                                                     const T* __restrict__ Kp,
                                                     const float* __restrict__ kc,
                                                     const int32_t* __restrict__ koff,
                                                     const int32_t* __restrict__ unit_prefix,
+                                                    const float* __restrict__ st2g,
                                                     int Nk, int Cq, int Ck, int maxu, float sl2,
                                                     float* __restrict__ rec) {
   constexpr int KC = D / 32;
   constexpr int LDR = D + 16 / sizeof(T);
-  constexpr bool kSplit = sizeof(T) == 2;
+  constexpr int QD = D / 4;  // dims staged per thread (4 threads per key row)
   __shared__ __attribute__((aligned(16))) T ks[64 * LDR];
+  __shared__ __attribute__((aligned(16))) T kl[sizeof(T) == 2 ? 64 * LDR : 8];
 
-  const int h = blockIdx.y, u = blockIdx.x, grp = blockIdx.z, tid = threadIdx.x;
-  const int32_t* up = unit_prefix + size_t(h) * (Ck + 1);
-  if (u >= up[Ck]) return;
-  const int cc = find_unit_cluster(up, Ck, u);
-  const int32_t* ko = koff + size_t(h) * (Ck + 1);
-  const int j0 = ko[cc] + (u - up[cc]) * kProbeUnit;
-  const int j1 = min(ko[cc + 1], j0 + kProbeUnit);
+  const int h = blockIdx.y, grp = blockIdx.z, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int32_t* up = unit_prefix + size_t(h) * (Ck + 1);
+  const int32_t* ko = koff + size_t(h) * (Ck + 1);
+  const int nunits = up[Ck];
 
-  Frag<T> bhi[2][KC], blo[2][KC];
-  float st[2];
-  const float* kbar = kc + (size_t(h) * Ck + cc) * D;
+  // centroid blocks of this wave: block w and w + 4 of the group's 8. For bf16
+  // the f32 centroid enters as a bf16 high part plus a bf16 remainder (about 16
+  // significant bits), two products accumulated in f32.
+  constexpr bool kSplit = sizeof(T) == 2;
+  Frag<T> bq[2][KC], bl[2][KC];
+  int cidx[2];
+  bool cok[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const int c = grp * kProbeGroup + w * 32 + cb * 16 + r;
-    const bool ok = c < Cq;
-    float dot = 0.f;
+    const int c = grp * kProbeGroup + (w + 4 * cb) * 16 + r;
+    cidx[cb] = c;
+    cok[cb] = c < Cq;
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
-      float x[8], val[8];
-      const float* qrow = qc + (size_t(h) * Cq + (ok ? c : 0)) * D + k * 32 + g * 8;
+      const float* qrow = qc + (size_t(h) * Cq + (cok[cb] ? c : 0)) * D + k * 32 + g * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = ok ? qrow[e] : 0.f;
-      split_centroid<T>(x, bhi[cb][k], blo[cb][k], val);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot = fmaf(val[e], kbar[k * 32 + g * 8 + e], dot);
+      for (int e = 0; e < 8; ++e) {
+        const float x = cok[cb] ? qrow[e] : 0.f;
+        bq[cb][k].v[e] = from_f32<T>(x);
+        bl[cb][k].v[e] = from_f32<T>(x - to_f32(bq[cb][k].v[e]));
+      }
     }
-    dot += __shfl_xor(dot, 16, 64);
-    dot += __shfl_xor(dot, 32, 64);
-    st[cb] = dot * sl2;
   }
-
-  float m[2], Z[2], E[2], e2[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) { m[cb] = st[cb]; Z[cb] = 0.f; E[cb] = 0.f; e2[cb] = 1.f; }
+  // blocks that hold no centroid skip their matrix work (wave-uniform)
+  const bool blk_live[2] = {grp * kProbeGroup + w * 16 < Cq, grp * kProbeGroup + (w + 4) * 16 < Cq};
 
   const T* Kh = Kp + size_t(h) * Nk * D;
-  constexpr int EPT = 16 / sizeof(T);
-  constexpr int CPR = D / EPT;
-  for (int tj = j0; tj < j1; tj += 64) {
-    __syncthreads();
-    for (int i = tid; i < 64 * CPR; i += 256) {
-      const int row = i / CPR, piece = i % CPR;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (tj + row < j1) v = *reinterpret_cast<const uint4*>(Kh + size_t(tj + row) * D + piece * EPT);
-      *reinterpret_cast<uint4*>(&ks[row * LDR + piece * EPT]) = v;
+  const int srow = tid >> 2, sq = tid & 3;
+
+  for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
+    const int cc = find_unit_cluster(up, Ck, u);
+    const int j0 = ko[cc] + (u - up[cc]) * kProbeUnit;
+    const int j1 = min(ko[cc + 1], j0 + kProbeUnit);
+    float kb[QD];  // this thread's quarter of the key centroid row
+    {
+      const float* kr = kc + (size_t(h) * Ck + cc) * D + sq * QD;
+#pragma unroll
+      for (int i = 0; i < QD; i += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(kr + i);
+        kb[i] = v.x; kb[i + 1] = v.y; kb[i + 2] = v.z; kb[i + 3] = v.w;
+      }
     }
-    __syncthreads();
-    const int nvalid = min(64, j1 - tj);
-    for (int kb = 0; kb * 16 < nvalid; ++kb) {
-      Frag<T> a[KC];
+    float st[2], mp[2], Z[2], E[2], e2[2];
 #pragma unroll
-      for (int k = 0; k < KC; ++k) a[k] = load8(&ks[(kb * 16 + r) * LDR + k * 32 + g * 8]);
+    for (int cb = 0; cb < 2; ++cb) {
+      st[cb] = cok[cb] ? st2g[(size_t(h) * Cq + cidx[cb]) * Ck + cc] : 0.f;
+      mp[cb] = 0.f;  // reference relative to s~: m = s~ + mp, mp >= 0
+      Z[cb] = 0.f;
+      E[cb] = 0.f;
+      e2[cb] = 1.f;
+    }
+    for (int tj = j0; tj < j1; tj += 64) {
+      __syncthreads();
+      {  // stage (k - kbar) as T high part + T remainder; rows past the unit are zero
+        const bool ok = tj + srow < j1;
+        const T* src = Kh + size_t(ok ? tj + srow : 0) * D + sq * QD;
+        T* dst = ks + srow * LDR + sq * QD;
+        T* dlo = kl + srow * LDR + sq * QD;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < QD; i += 16 / sizeof(T)) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(src + i);
+          const T* el = reinterpret_cast<const T*>(&raw);
+          T out[16 / sizeof(T)], rem[16 / sizeof(T)];
+#pragma unroll
+          for (int e = 0; e < int(16 / sizeof(T)); ++e) {
+            const float dlt = ok ? to_f32(el[e]) - kb[i + e] : 0.f;
+            out[e] = from_f32<T>(dlt);
+            rem[e] = from_f32<T>(dlt - to_f32(out[e]));
+          }
+          *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(out);
+          if (kSplit) *reinterpret_cast<uint4*>(dlo + i) = *reinterpret_cast<const uint4*>(rem);
+        }
+      }
+      __syncthreads();
+      const int nvalid = min(64, j1 - tj);
+      for (int kb16 = 0; kb16 * 16 < nvalid; ++kb16) {
+        Frag<T> a[KC], al[KC];
 #pragma unroll
         for (int k = 0; k < KC; ++k) {
-          mma(acc, a[k], bhi[cb][k]);
-          if (kSplit) mma(acc, a[k], blo[cb][k]);
-        }
-        float s2[4];
-        float tmax = -__builtin_inff();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = kb * 16 + g * 4 + i < nvalid;
-          s2[i] = ok ? acc[i] * sl2 : -__builtin_inff();
-          tmax = fmaxf(tmax, s2[i]);
-        }
-        if (tmax > m[cb]) {
-          const float al = fast_exp2(m[cb] - tmax);
-          Z[cb] *= al;
-          E[cb] *= al * al;
-          m[cb] = tmax;
-          e2[cb] = fast_exp2(st[cb] - tmax);
+          a[k] = load8(&ks[(kb16 * 16 + r) * LDR + k * 32 + g * 8]);
+          if (kSplit) al[k] = load8(&kl[(kb16 * 16 + r) * LDR + k * 32 + g * 8]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (kb * 16 + g * 4 + i < nvalid) {
-            const float e = fast_exp2(s2[i] - m[cb]);
-            Z[cb] += e;
-            const float dd = e - e2[cb];
-            E[cb] = fmaf(dd, dd, E[cb]);
+        for (int cb = 0; cb < 2; ++cb) {
+          if (!blk_live[cb]) continue;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          // (qhi + qlo).(dhi + dlo) without the qlo.dlo term (below 2^-16 relative)
+#pragma unroll
+          for (int k = 0; k < KC; ++k) {
+            mma(acc, a[k], bq[cb][k]);
+            if (kSplit) {
+              mma(acc, a[k], bl[cb][k]);
+              mma(acc, al[k], bq[cb][k]);
+            }
+          }
+          // lane holds delta for keys kb16*16 + 4g + i of centroid cidx[cb]
+          float d2[4];
+          float tmax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = kb16 * 16 + g * 4 + i < nvalid;
+            d2[i] = ok ? acc[i] * sl2 : -__builtin_inff();
+            tmax = fmaxf(tmax, d2[i]);
+          }
+          if (tmax > mp[cb]) {
+            const float al = fast_exp2(mp[cb] - tmax);
+            Z[cb] *= al;
+            E[cb] *= al * al;
+            mp[cb] = tmax;
+            e2[cb] = fast_exp2(-tmax);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (kb16 * 16 + g * 4 + i < nvalid) {
+              const float e = fast_exp2(d2[i] - mp[cb]);
+              Z[cb] += e;
+              const float dd = e - e2[cb];
+              E[cb] = fmaf(dd, dd, E[cb]);
+            }
           }
         }
       }
     }
-  }
-
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const float om = __shfl_xor(m[cb], o, 64);
-      const float oZ = __shfl_xor(Z[cb], o, 64);
-      const float oE = __shfl_xor(E[cb], o, 64);
-      const float M = fmaxf(m[cb], om);
-      const float a1 = fast_exp2(m[cb] - M), a2 = fast_exp2(om - M);
-      Z[cb] = Z[cb] * a1 + oZ * a2;
-      E[cb] = E[cb] * (a1 * a1) + oE * (a2 * a2);
-      m[cb] = M;
-    }
-    const int c = grp * kProbeGroup + w * 32 + cb * 16 + r;
-    if (g == 0 && c < Cq) {
-      float* o = rec + ((size_t(h) * maxu + u) * Cq + c) * 3;
-      o[0] = m[cb];
-      o[1] = Z[cb];
-      o[2] = E[cb];
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float om = __shfl_xor(mp[cb], o, 64);
+        const float oZ = __shfl_xor(Z[cb], o, 64);
+        const float oE = __shfl_xor(E[cb], o, 64);
+        const float M = fmaxf(mp[cb], om);
+        const float a1 = fast_exp2(mp[cb] - M), a2 = fast_exp2(om - M);
+        Z[cb] = Z[cb] * a1 + oZ * a2;
+        E[cb] = E[cb] * (a1 * a1) + oE * (a2 * a2);
+        mp[cb] = M;
+      }
+      if (g == 0 && cok[cb]) {
+        float* o = rec + ((size_t(h) * maxu + u) * Cq + cidx[cb]) * 3;
+        o[0] = st[cb] + mp[cb];  // absolute base-2 reference of this unit
+        o[1] = Z[cb];
+        o[2] = E[cb];
+      }
     }
   }
 }
@@ -244,34 +284,52 @@ __global__ __launch_bounds__(256) void probe_finalize_kernel(int Cq, int Ck, int
   if (tid == 0 && log_norm) log_norm[size_t(h) * Cq + c] = (m + __log2f(Z)) * 0.69314718055994530942f;
 }
 
+size_t probe_ws_bytes(int H, int Nk, int Cq, int Ck) {
+  return align256(sizeof(int32_t) * size_t(H) * (Ck + 1)) +
+         align256(sizeof(float) * size_t(H) * Cq * Ck) +
+         align256(sizeof(float) * 3 * size_t(H) * max_units(Nk, Ck) * Cq);
+}
+
 template <typename T, int D>
-static void probe_t(int H, int Nk, int Cq, int Ck, float sl2, const float* qc, const void* Kp,
-                    const float* kc, const int32_t* koff, const int32_t* up, float* rec,
-                    hipStream_t s) {
+static hipError_t probe_t(int H, int Nk, int Cq, int Ck, float sl2, const float* qc,
+                          const void* Kp, const float* kc, const int32_t* koff, const int32_t* up,
+                          float* st2, float* rec, hipStream_t s) {
+  hipLaunchKernelGGL((centroid_logits_kernel<D>), dim3(ceil_div(Ck, 16), ceil_div(Cq, 16), H),
+                     dim3(256), 0, s, Cq, Ck, sl2, qc, kc, st2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int maxu = max_units(Nk, Ck);
-  hipLaunchKernelGGL((probe_kernel<T, D>), dim3(maxu, H, ceil_div(Cq, kProbeGroup)), dim3(256), 0,
-                     s, qc, static_cast<const T*>(Kp), kc, koff, up, Nk, Cq, Ck, maxu, sl2, rec);
+  const int groups = ceil_div(Cq, kProbeGroup);
+  int per_head = ceil_div(2048, H * groups);
+  per_head = per_head < 1 ? 1 : (per_head > maxu ? maxu : per_head);
+  hipLaunchKernelGGL((probe_kernel<T, D>), dim3(per_head, H, groups), dim3(256), 0, s, qc,
+                     static_cast<const T*>(Kp), kc, koff, up, st2, Nk, Cq, Ck, maxu, sl2, rec);
+  return hipGetLastError();
 }
 
 hipError_t launch_probe(int elem_bytes, int H, int Nk, int d, int Cq, int Ck, float scale,
                         const float* qc, const void* Kp, const float* kc, const int32_t* koff,
-                        int32_t* unit_prefix, float* rec, float* ratio, float* log_norm,
-                        hipStream_t s) {
-  hipLaunchKernelGGL(probe_units_kernel, dim3(H), dim3(1024), 0, s, Ck, koff, unit_prefix);
+                        void* ws, float* ratio, float* log_norm, hipStream_t s) {
+  char* p = static_cast<char*>(ws);
+  int32_t* up = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * size_t(H) * (Ck + 1));
+  float* st2 = reinterpret_cast<float*>(p);
+  p += align256(sizeof(float) * size_t(H) * Cq * Ck);
+  float* rec = reinterpret_cast<float*>(p);
+  hipLaunchKernelGGL(probe_units_kernel, dim3(H), dim3(1024), 0, s, Ck, koff, up);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float sl2 = scale * 1.44269504088896340736f;
   if (elem_bytes == 2) {
-    if (d == 128) probe_t<__bf16, 128>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, unit_prefix, rec, s);
-    else probe_t<__bf16, 64>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, unit_prefix, rec, s);
+    e = (d == 128) ? probe_t<__bf16, 128>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, rec, s)
+                   : probe_t<__bf16, 64>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, rec, s);
   } else {
-    if (d == 128) probe_t<float, 128>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, unit_prefix, rec, s);
-    else probe_t<float, 64>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, unit_prefix, rec, s);
+    e = (d == 128) ? probe_t<float, 128>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, rec, s)
+                   : probe_t<float, 64>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, rec, s);
   }
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(probe_finalize_kernel, dim3(Cq, H), dim3(256), 0, s, Cq, Ck,
-                     max_units(Nk, Ck), koff, unit_prefix, rec, ratio, log_norm);
+                     max_units(Nk, Ck), koff, up, rec, ratio, log_norm);
   return hipGetLastError();
 }
 

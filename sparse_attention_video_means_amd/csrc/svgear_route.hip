@@ -56,16 +56,33 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ ra
       __syncthreads();
     }
   }
-  if (tid == 0) {
-    int used = 0;
-    for (int i = 0; i < Ck; ++i) {
-      const uint64_t k = key[i];
-      if (k == ~0ull || used == budget) break;
-      const int id = int(uint32_t(k));
-      const int n = cnt[id];
-      if (used + n <= budget) { sel[id] = 1; used += n; }
+  // Greedy fill by wavefront 0, 64 candidates at a time: within a window the
+  // first candidate (in order) that fits is taken, the budget shrinks, and the
+  // search resumes after it. Candidates passed over did not fit when their turn
+  // came and the remaining budget only shrinks, so this is the same walk as a
+  // one-at-a-time loop.
+  if (tid < 64) {
+    const int lane = tid;
+    int rem = budget;
+    for (int base = 0; base < Ck && rem > 0; base += 64) {
+      const int i = base + lane;
+      const uint64_t k = (i < Ck) ? key[i] : ~0ull;
+      const bool valid = k != ~0ull;
+      const int id = valid ? int(uint32_t(k)) : 0;
+      const int n = valid ? cnt[id] : 0;
+      uint64_t pending = __ballot(valid);
+      while (pending) {
+        const uint64_t fits = __ballot(valid && n <= rem) & pending;
+        if (!fits) break;
+        const int f = __ffsll((unsigned long long)fits) - 1;
+        const int nf = __shfl(n, f, 64);
+        if (lane == f) sel[id] = 1;
+        rem -= nf;
+        pending &= (f == 63) ? 0ull : (~0ull << (f + 1));
+      }
+      if (__ballot(!valid)) break;  // the sorted keys of empty clusters start here
     }
-    used_s = used;
+    if (lane == 0) used_s = budget - rem;
   }
   __syncthreads();
   uint8_t* mk = mask + (size_t(h) * Cq + c) * Ck;

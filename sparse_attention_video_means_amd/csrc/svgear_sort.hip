@@ -24,6 +24,7 @@ size_t sort_ws_bytes(int H, int N, int d, int C, int ntensors) {
   b += align256(sizeof(int32_t) * size_t(H) * N);
   b += align256(sizeof(int32_t) * size_t(H) * C * sort_tiles(N));
   b += align256(sizeof(int32_t) * size_t(H) * (C + 1));
+  b += align256(sizeof(int32_t) * size_t(H) * C);
   b += align256(sizeof(float) * size_t(H) * ntensors * max_chunks(N, C) * d);
   return b;
 }
@@ -37,6 +38,8 @@ SortWs sort_ws_carve(void* ws, int H, int N, int d, int C, int ntensors) {
   p += align256(sizeof(int32_t) * size_t(H) * C * sort_tiles(N));
   w.chunk_prefix = reinterpret_cast<int32_t*>(p);
   p += align256(sizeof(int32_t) * size_t(H) * (C + 1));
+  w.sizes = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * size_t(H) * C);
   w.partial = reinterpret_cast<float*>(p);
   return w;
 }
@@ -59,54 +62,63 @@ __global__ __launch_bounds__(256) void label_rank_kernel(const int32_t* __restri
         wave_hist[c] + wave_hist[C + c] + wave_hist[2 * C + c] + wave_hist[3 * C + c];
 }
 
-__global__ __launch_bounds__(1024) void sort_scan_kernel(int N, int C, int tiles,
-                                                         int32_t* __restrict__ hist,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ chunk_prefix) {
-  __shared__ int scratch[16];
-  __shared__ int off_s[kMaxClusters + 1];
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const size_t E = size_t(C) * tiles;
-  int32_t* base = hist + size_t(h) * E;
+// Per (head, cluster): exclusive prefix of the cluster's tile counts, in
+// place, and the cluster's size. One wavefront per cluster row.
+__global__ __launch_bounds__(256) void tile_prefix_kernel(int C, int tiles,
+                                                          int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ sizes) {
+  const int h = blockIdx.y, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= C) return;
+  int32_t* row = hist + (size_t(h) * C + c) * tiles;
   int carry = 0;
-  for (size_t r0 = 0; r0 < E; r0 += 1024) {
-    const size_t idx = r0 + tid;
-    const int v = idx < E ? base[idx] : 0;
-    int tot;
-    const int ex = block_exclusive_scan(v, scratch, &tot);
-    if (idx < E) {
-      base[idx] = carry + ex;
-      if (idx % tiles == 0) off_s[idx / tiles] = carry + ex;
-    }
-    carry += tot;
+  for (int t0 = 0; t0 < tiles; t0 += 64) {
+    const int t = t0 + lane;
+    const int v = t < tiles ? row[t] : 0;
+    const int inc = wave_inclusive_scan(v);
+    if (t < tiles) row[t] = carry + inc - v;
+    carry += __shfl(inc, 63, 64);
   }
-  if (tid == 0) off_s[C] = carry;
-  __syncthreads();
-  int chunks = 0;
-  if (tid < C) {
-    const int cnt = off_s[tid + 1] - off_s[tid];
-    offsets[size_t(h) * (C + 1) + tid] = off_s[tid];
-    if (counts) counts[size_t(h) * C + tid] = cnt;
-    chunks = (cnt + kChunk - 1) / kChunk;
-  }
-  if (tid == 0) offsets[size_t(h) * (C + 1) + C] = off_s[C];
+  if (lane == 0) sizes[size_t(h) * C + c] = carry;
+}
+
+// Per head: cluster offsets and the chunk list of the segment sums.
+__global__ __launch_bounds__(1024) void cluster_offsets_kernel(int C,
+                                                               const int32_t* __restrict__ sizes,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ chunk_prefix) {
+  __shared__ int scratch[16];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int cnt = tid < C ? sizes[size_t(h) * C + tid] : 0;
   int total;
-  const int ex = block_exclusive_scan(chunks, scratch, &total);
-  if (tid < C) chunk_prefix[size_t(h) * (C + 1) + tid] = ex;
-  if (tid == 0) chunk_prefix[size_t(h) * (C + 1) + C] = total;
+  const int ex = block_exclusive_scan(cnt, scratch, &total);
+  const int chunks = (cnt + kChunk - 1) / kChunk;
+  int ctotal;
+  const int cex = block_exclusive_scan(chunks, scratch, &ctotal);
+  if (tid < C) {
+    offsets[size_t(h) * (C + 1) + tid] = ex;
+    if (counts) counts[size_t(h) * C + tid] = cnt;
+    chunk_prefix[size_t(h) * (C + 1) + tid] = cex;
+  }
+  if (tid == 0) {
+    offsets[size_t(h) * (C + 1) + C] = total;
+    chunk_prefix[size_t(h) * (C + 1) + C] = ctotal;
+  }
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ labels,
                                                       const int32_t* __restrict__ rank,
-                                                      const int32_t* __restrict__ base, int N,
+                                                      const int32_t* __restrict__ tpre,
+                                                      const int32_t* __restrict__ offsets, int N,
                                                       int C, int tiles,
                                                       int32_t* __restrict__ perm) {
   const int h = blockIdx.y, t = blockIdx.x;
   const int n = t * kTile + threadIdx.x;
   if (n >= N) return;
   const int lab = min(max(labels[size_t(h) * N + n], 0), C - 1);
-  const int p = base[(size_t(h) * C + lab) * tiles + t] + rank[size_t(h) * N + n];
+  const int p = offsets[size_t(h) * (C + 1) + lab] + tpre[(size_t(h) * C + lab) * tiles + t] +
+                rank[size_t(h) * N + n];
   perm[size_t(h) * N + p] = n;
 }
 
@@ -152,13 +164,25 @@ __global__ __launch_bounds__(256) void segsum_kernel(int N, int C, int nt, int m
     float acc[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
-    for (int p = p0 + rg; p < p1; p += RPI) {
-      const int row = perm[size_t(h) * N + p];
-      uint4 v = *reinterpret_cast<const uint4*>(s + size_t(row) * D + col * EPT);
-      if (dd) *reinterpret_cast<uint4*>(dd + size_t(p) * D + col * EPT) = v;
-      const T* el = reinterpret_cast<const T*>(&v);
+    // four rows in flight per thread; rows are still added in slot order
+    constexpr int U = 4;
+    for (int p = p0 + rg; p < p1; p += U * RPI) {
+      int row[U];
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) acc[e] += to_f32(el[e]);
+      for (int u = 0; u < U; ++u) row[u] = (p + u * RPI < p1) ? perm[size_t(h) * N + p + u * RPI] : -1;
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = row[u] >= 0 ? *reinterpret_cast<const uint4*>(s + size_t(row[u]) * D + col * EPT)
+                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (row[u] < 0) break;
+        if (dd) *reinterpret_cast<uint4*>(dd + size_t(p + u * RPI) * D + col * EPT) = v[u];
+        const T* el = reinterpret_cast<const T*>(&v[u]);
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) acc[e] += to_f32(el[e]);
+      }
     }
 #pragma unroll
     for (int e = 0; e < EPT; ++e) red[rg][col * EPT + e] = acc[e];
@@ -232,18 +256,23 @@ hipError_t launch_label_rank(const int32_t* labels, int H, int N, int C, int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_sort_scan(int H, int N, int C, int32_t* hist, int32_t* offsets,
+hipError_t launch_sort_scan(int H, int N, int C, int32_t* hist, int32_t* sizes, int32_t* offsets,
                             int32_t* counts, int32_t* chunk_prefix, hipStream_t s) {
-  hipLaunchKernelGGL(sort_scan_kernel, dim3(H), dim3(1024), 0, s, N, C, sort_tiles(N), hist,
-                     offsets, counts, chunk_prefix);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(ceil_div(C, 4), H), dim3(256), 0, s, C,
+                     sort_tiles(N), hist, sizes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cluster_offsets_kernel, dim3(H), dim3(1024), 0, s, C, sizes, offsets, counts,
+                     chunk_prefix);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const int32_t* labels, const int32_t* rank, const int32_t* hist,
-                          int H, int N, int C, int32_t* perm, hipStream_t s) {
+                          const int32_t* offsets, int H, int N, int C, int32_t* perm,
+                          hipStream_t s) {
   const int tiles = sort_tiles(N);
-  hipLaunchKernelGGL(scatter_kernel, dim3(tiles, H), dim3(256), 0, s, labels, rank, hist, N, C,
-                     tiles, perm);
+  hipLaunchKernelGGL(scatter_kernel, dim3(tiles, H), dim3(256), 0, s, labels, rank, hist, offsets,
+                     N, C, tiles, perm);
   return hipGetLastError();
 }
 

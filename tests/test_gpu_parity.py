@@ -184,7 +184,16 @@ def test_probe_against_oracle(name):
         ok = probe_tol(got, ratio)
         assert ok.all(), f"{(~ok).sum()} of {ok.size} ratios off; worst " \
                          f"{np.max(np.abs(got - ratio) / (np.abs(ratio) + 1e-30))}"
-        np.testing.assert_allclose(f64(res["log_norm"][h]), log_norm, rtol=0, atol=2e-4)
+        # log_norm moves by at most max_j |error of s_cj|; the kernel carries
+        # qbar and (k_j - kbar) as bf16 high part + remainder (about 2^-16
+        # relative per factor) and accumulates in f32, so
+        # |error| <= scale * 2^-14 * sum_d |qbar_d (k_jd - kbar_d)| + f32 rounding.
+        qb, kp, kb = f64(res["q_bar"][h]), f64(res["kp"][h]), f64(res["k_bar"][h])
+        koff = f64(res["k_off"][h])
+        dk = np.abs(kp - np.repeat(kb, np.diff(koff), axis=0))
+        unit = 2.0 ** -14 if wl.dtype == "bf16" else 2.0 ** -20
+        bound = (1 / math.sqrt(wl.d)) * unit * (np.abs(qb) @ dk.T).max(axis=1) + 2e-5
+        assert np.all(np.abs(f64(res["log_norm"][h]) - log_norm) <= bound)
 
 
 @pytest.mark.parametrize("name", list(CASES))
