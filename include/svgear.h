@@ -20,6 +20,8 @@
  *    (float) or SVGEAR_BF16 (bfloat16 stored as uint16). Centroid tables,
  *    ratios and normalisers are always float32.
  *  - Supported head dimension d: 64 or 128. Cluster counts: 1 <= C <= min(N, 1024).
+ *    One head holds fewer than 2^31 elements (N*d < 2^31) and all heads
+ *    together at most 2^40.
  *  - Ownership: the caller allocates and frees every buffer, including the
  *    workspace; the library never allocates, frees or synchronises. Work is
  *    enqueued on the caller's stream `s` (0 = the legacy default stream) and

@@ -21,6 +21,7 @@ svgear_status check_shape(svgear_dtype dt, int H, int N, int d, int C) {
   if (H < 1 || N < 1 || C < 1 || C > N || C > kMaxClusters) return SVGEAR_ERR_INVALID_ARG;
   if (elem_bytes(dt) == 0 || !dim_ok(d)) return SVGEAR_ERR_UNSUPPORTED;
   if (size_t(H) * N * d > (size_t(1) << 40)) return SVGEAR_ERR_INVALID_ARG;
+  if (size_t(N) * d >= (size_t(1) << 31)) return SVGEAR_ERR_INVALID_ARG;  // 32-bit row offsets
   return SVGEAR_OK;
 }
 

@@ -3,115 +3,140 @@
 // exact keys of its selected key clusters and one centroid logit (+ ln|k_c'|)
 // per skipped non-empty key cluster, with mean values for the latter.
 //
-// Block = 4 wavefronts x (16*QB) queries of one query cluster. The selected key
-// clusters are packed back to back into 64-key tiles (a tile may span several
-// clusters, so ragged cluster ends waste no matrix work); the skipped clusters'
-// centroid rows (pre-rounded to the element type) follow as further 64-row
-// tiles carrying the log2|k_c'| bias. Both kinds of tile run through the same
-// online softmax:
-//   S^T = K Q^T     (A = K rows from LDS, B = Q^T held in registers)
-//   O^T += V^T P^T  (A = V^T read from row-major LDS with ds_read_b64_tr_b16,
-//                    B = P^T taken straight from the S^T accumulators)
+// Block = NW wavefronts x (16*QB) queries of one query cluster. The selected
+// key clusters are packed back to back into 64-key tiles (a tile may span
+// several clusters, so ragged cluster ends waste no matrix work); the skipped
+// clusters' centroid rows (pre-rounded to the element type) follow as further
+// 64-row tiles carrying the log|k_c'| bias. Both kinds of tile run through the
+// same online softmax:
+//   S^T = K Q^T     (A = K fragments from LDS, B = Q^T held in registers)
+//   O^T += V^T P^T  (A = V^T fragments from LDS, B = P^T taken straight from
+//                    the S^T accumulators)
 // so P never leaves registers.
 //
-// Tiles are double-buffered in LDS and filled by global_load_lds_dwordx4: each
-// lane's 16-byte piece lands at (LDS pointer + 16 * lane), so no registers are
-// spent on staging. Rows are stored unpadded with their 16-byte pieces XOR-
-// swizzled by a function of the row, chosen so that both the K reads (16 rows,
-// same piece) and the transposed V reads (8 rows, two adjacent pieces) hit
-// distinct LDS banks. The loads of tile t+1 are issued before tile t is
-// computed; one wait and one barrier per tile.
+// LDS layout. Tiles are double-buffered and filled by global_load_lds_dwordx4,
+// which puts lane l's 16-byte piece at (LDS pointer + 16 l) while its global
+// address is free. The copy therefore writes every piece where the matrix
+// operands will read it: for bf16, K in MFMA fragment order (one 1 KB
+// fragment per 16 keys x 32 dims, lane order) and V in the order of the
+// transposing read ds_read_b64_tr_b16 (512 contiguous bytes per read), so
+// every LDS read of the inner loop is one contiguous, conflict-free block.
+// (f32 tiles, the reference-precision path, use plain row-major rows with
+// XOR-swizzled 16-byte pieces.) The loads of tile t+1 are issued before tile
+// t is computed; one wait and one barrier per tile. The source row of each
+// key of a tile is looked up once per lane and shared with a lane shuffle.
 //
-// Exponentials are base 2 with log2(e) folded into the scale; the running
-// maximum is only raised (and O, l rescaled) when a tile's maximum exceeds it
-// by more than 8, which keeps every p <= 2^8.
+// Softmax. Exponentials are base 2 with log2(e) folded into the scale. The
+// row biases (0 for exact keys, ln|k_c'| for centroid rows, -inf for filler)
+// seed the S accumulators, so every logit leaves the matrix core complete.
+// The running maximum m of a query is only raised when a logit exceeds it by
+// more than kRescaleSlack, so every weight stays below 2^kRescaleSlack; the
+// test uses each lane's own maximum (a row exceeds the bound exactly when one
+// of its lanes does), and the cross-lane row maximum and the O, l rescale are
+// only computed on the rare tiles that raise m.
+//
+// Per tile the two 32-key halves are skewed so that matrix and vector work
+// of different halves sit next to each other:
+//   S0 | S1 + exp(S0) | PV0 + exp(S1) | PV1
 #include "svgear_common.hpp"
 #include "svgear_internal.hpp"
 
 namespace svg {
 
-constexpr int kAttBK = 64;  // keys per tile
-constexpr float kRescaleSlack = 8.0f;
+constexpr int kAttBK = 64;              // keys per tile
+constexpr float kRescaleSlack = 16.0f;  // weights stay below 2^16 between rescales
 
 template <typename T>
 struct AttCfg;
-#ifndef SVGEAR_ATT_QB_BF16
-#define SVGEAR_ATT_QB_BF16 2
+#ifndef SVGEAR_ATT_NW
+#define SVGEAR_ATT_NW 8
 #endif
 template <>
 struct AttCfg<__bf16> {
-  static constexpr int QB = SVGEAR_ATT_QB_BF16;  // 16-query blocks per wavefront
+  static constexpr int QB = 2;              // 16-query blocks per wavefront
+  static constexpr int NW = SVGEAR_ATT_NW;  // wavefronts per block
 };
 template <>
 struct AttCfg<float> {
-  static constexpr int QB = 2;
+  static constexpr int QB = 1;
+  static constexpr int NW = 4;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Swizzle of the 16-byte pieces of one LDS row; CPR = pieces per row.
-template <int CPR>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (CPR == 16) {
-    return ((row & 7) << 1) | ((row >> 3) & 1);
-  } else if constexpr (CPR == 8) {
-    const int a = row >> 1;
-    return ((a & 3) << 1) | ((a >> 2) & 1);
-  } else {
-    return row & (CPR - 1);
-  }
-}
-
-// Element (row, col) of a swizzled tile.
+// Where the 16-byte piece slot j of a K or V tile comes from (key row of the
+// tile and 16-byte piece of that row), and how the matrix operands are read.
 template <typename T, int D>
-__device__ __forceinline__ int lds_index(int row, int col) {
-  constexpr int EPT = 16 / sizeof(T);
-  constexpr int CPR = D / EPT;
-  return row * D + (((col / EPT) ^ swz<CPR>(row)) * EPT) + (col % EPT);
-}
+struct TileLayout;
 
-// A operand K (16 keys x 32 dims): lane (r, g) holds K[row0 + r][k*32 + g*8 .. +7].
+// bf16: fragment-ordered K, transposed-read-ordered V.
 template <int D>
-__device__ __forceinline__ Frag<__bf16> load_k(const __bf16* ks, int row, int k, int g) {
-  return load8(ks + lds_index<__bf16, D>(row, k * 32 + g * 8));
-}
-
-template <int D>
-__device__ __forceinline__ Frag<float> load_k(const float* ks, int row, int k, int g) {
-  Frag<float> f;
-  const float4 a = *reinterpret_cast<const float4*>(ks + lds_index<float, D>(row, k * 32 + g * 8));
-  const float4 b = *reinterpret_cast<const float4*>(ks + lds_index<float, D>(row, k * 32 + g * 8 + 4));
-  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
-  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
-  return f;
-}
-
-// A operand V^T (16 dims x 32 keys) for key chunk kc2 and dim block db; key
-// slot e of lane (r, g) is tile row 32*kc2 + 4g + (e < 4 ? e : 12 + e).
-template <int D>
-__device__ __forceinline__ Frag<__bf16> load_vt(const __bf16* vs, int kc2, int db, int r, int g) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  const int row = kc2 * 32 + g * 4 + (r >> 2);
-  const int col = db * 16 + (r & 3) * 4;
-  const bf16x4 lo =
-      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vs + lds_index<__bf16, D>(row, col)));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-      (lds_bf16x4*)(vs + lds_index<__bf16, D>(row + 16, col)));
-  Frag<__bf16> f;
-  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return f;
-}
-
-template <int D>
-__device__ __forceinline__ Frag<float> load_vt(const float* vs, int kc2, int db, int r, int g) {
-  Frag<float> f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int key = kc2 * 32 + g * 4 + (e < 4 ? e : 12 + e);
-    f.v[e] = vs[lds_index<float, D>(key, db * 16 + r)];
+struct TileLayout<__bf16, D> {
+  static constexpr int KC = D / 32;  // 32-dim chunks (K fragments per 16 keys)
+  static constexpr int DB = D / 16;  // 16-dim blocks (V^T fragments per 32 keys)
+  // fragment f = (16-key block rb, chunk k) occupies slots 64f .. 64f+63 in
+  // lane order: lane (r, g) holds K[16 rb + r][32 k + 8 g .. +7]
+  __device__ static void k_slot(int j, int& row, int& piece) {
+    const int f = j >> 6, l = j & 63;
+    row = (f / KC) * 16 + (l & 15);
+    piece = (f % KC) * 4 + (l >> 4);
   }
-  return f;
-}
+  // transposed read (32-key half h, dim block db, upper 16 keys u) occupies
+  // slots 32 i .. 32 i + 31, i = (h DB + db) 2 + u; lane group g of the read
+  // takes keys 32 h + 16 u + 4 g + e (e = 0..3), 16 dims each, as two pieces
+  __device__ static void v_slot(int j, int& row, int& piece) {
+    const int i = j >> 5, q = j & 31;
+    const int u = i & 1, db = (i >> 1) % DB, h = (i >> 1) / DB;
+    row = h * 32 + u * 16 + 4 * (q >> 3) + ((q & 7) >> 1);
+    piece = 2 * db + (q & 1);
+  }
+  // A operand K (16 keys x 32 dims) of block rb, chunk k
+  __device__ static Frag<__bf16> k_frag(const __bf16* ks, int rb, int k, int lane) {
+    return load8(ks + (rb * KC + k) * 512 + lane * 8);
+  }
+  // A operand V^T (16 dims x 32 keys) of half h, dim block db; key slot e of
+  // lane (r, g) is tile key 32 h + 4 g + (e < 4 ? e : 12 + e)
+  __device__ static Frag<__bf16> vt_frag(const __bf16* vs, int h, int db, int lane) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const __bf16* p = vs + (h * DB + db) * 512 + lane * 4;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 256));
+    Frag<__bf16> f;
+    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+  }
+};
+
+// f32: row-major rows whose 16-byte pieces are XOR-swizzled by the row.
+template <int D>
+struct TileLayout<float, D> {
+  static constexpr int CPR = D / 4;  // pieces per row
+  __device__ static int swz(int row) { return row & (CPR - 1); }
+  __device__ static int index(int row, int col) {
+    return row * D + (((col >> 2) ^ swz(row)) << 2) + (col & 3);
+  }
+  __device__ static void k_slot(int j, int& row, int& piece) {
+    row = j / CPR;
+    piece = (j % CPR) ^ swz(row);
+  }
+  __device__ static void v_slot(int j, int& row, int& piece) { k_slot(j, row, piece); }
+  __device__ static Frag<float> k_frag(const float* ks, int rb, int k, int lane) {
+    const int row = rb * 16 + (lane & 15), col = k * 32 + (lane >> 4) * 8;
+    Frag<float> f;
+    const float4 a = *reinterpret_cast<const float4*>(ks + index(row, col));
+    const float4 b = *reinterpret_cast<const float4*>(ks + index(row, col + 4));
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+    return f;
+  }
+  __device__ static Frag<float> vt_frag(const float* vs, int h, int db, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    Frag<float> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = vs[index(h * 32 + g * 4 + (e < 4 ? e : 12 + e), db * 16 + r)];
+    return f;
+  }
+};
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, const float (&v)[4]);
@@ -126,6 +151,23 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* p, const float (&v)[4]) {
 template <>
 __device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// acc + sum of the eight elements of a fragment (bf16: four v_dot2 with ones).
+__device__ __forceinline__ float frag_sum(const Frag<__bf16>& f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {__bf16(1.0f), __bf16(1.0f)};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.v, f.v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.v, f.v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.v, f.v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f.v, f.v, 6, 7), one, acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ float frag_sum(const Frag<float>& f, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc += f.v[e];
+  return acc;
 }
 
 // max / sum of x over lanes l, l^16, l^32, l^48 (VALU lane swaps, no LDS).
@@ -144,19 +186,23 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void attend_kernel(
+__global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_kernel(
     const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
     const int32_t* __restrict__ qoff, const int32_t* __restrict__ koff,
     const T* __restrict__ kcen, const T* __restrict__ vcen, const uint8_t* __restrict__ mask,
-    int Nq, int Nk, int Cq, int Ck, float sl2, T* __restrict__ Op) {
+    int H, int Nq, int Nk, int Cq, int Ck, float sl2, int per_head, int span,
+    T* __restrict__ Op) {
+  using L = TileLayout<T, D>;
   constexpr int QB = AttCfg<T>::QB;
-  constexpr int BM = 64 * QB;
+  constexpr int NW = AttCfg<T>::NW;
+  constexpr int BM = 16 * NW * QB;
   constexpr int KC = D / 32;
   constexpr int DB = D / 16;
   constexpr int EPT = 16 / sizeof(T);
-  constexpr int CPR = D / EPT;       // 16-byte pieces per row
-  constexpr int NI = CPR / 4;        // load instructions per wave per tensor per tile
-  constexpr int TILE = kAttBK * D;   // elements per tile
+  constexpr int PIECES = kAttBK * D / EPT;  // 16-byte pieces per tile and tensor
+  constexpr int NI = PIECES / (64 * NW);    // copy instructions per wave, tensor and tile
+  static_assert(NI * 64 * NW == PIECES, "tile pieces must split evenly over the waves");
+  constexpr int TILE = kAttBK * D;          // elements per tile
   // two buffers per tensor as distinct objects: the compiler can then tell
   // the asynchronous fill of one from the reads of the other and inserts no
   // wait between them
@@ -164,26 +210,32 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
   __shared__ __attribute__((aligned(16))) T ks1[TILE];
   __shared__ __attribute__((aligned(16))) T vs0[TILE];
   __shared__ __attribute__((aligned(16))) T vs1[TILE];
-  __shared__ float bias0[kAttBK];
-  __shared__ float bias1[kAttBK];
+  __shared__ __attribute__((aligned(16))) float bias0[kAttBK];
+  __shared__ __attribute__((aligned(16))) float bias1[kAttBK];
   // per-block lists, sized by Ck at launch (5 * Ck + 1 words):
   extern __shared__ int lists[];
   int* sel_s = lists;                  // selected key cluster ids, ascending
   int* start_s = lists + Ck;           // first key row of a selection minus its packed offset
   int* comp_s = lists + 2 * Ck;        // compensated (skipped, non-empty) key clusters
-  float* cbias_s = reinterpret_cast<float*>(lists + 3 * Ck);  // log2 |k_c'| of those
+  float* cbias_s = reinterpret_cast<float*>(lists + 3 * Ck);  // ln |k_c'| / scale of those
   int* pref_s = lists + 4 * Ck;        // packed offset of every selected cluster (+ total)
   __shared__ int scratch[16];
   __shared__ int info[2];
 
-  const int h = blockIdx.y, t = blockIdx.x, tid = threadIdx.x;
+  // Blocks are dealt to the XCDs round-robin (block b runs on XCD b % 8).
+  // Renumber so that every XCD walks one contiguous range of (head, tile):
+  // the tiles of one query cluster then run side by side on one XCD and read
+  // the same key/value rows through its L2.
+  const int logical = int(blockIdx.x % kXcds) * span + int(blockIdx.x / kXcds);
+  const int h = logical / per_head, t = logical % per_head, tid = threadIdx.x;
+  if (h >= H) return;  // padding of the grid to a multiple of the XCD count
   const int w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int32_t* qo = qoff + size_t(h) * (Cq + 1);
   const int32_t* ko = koff + size_t(h) * (Ck + 1);
 
   // ---- which query cluster / tile this block owns
   int carry = 0;
-  for (int b = 0; b < Cq; b += 256) {
+  for (int b = 0; b < Cq; b += 64 * NW) {
     const int i = b + tid;
     const int nt = (i < Cq) ? (qo[i + 1] - qo[i] + BM - 1) / BM : 0;
     int tot;
@@ -203,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
   // ---- selected (packed) and compensated key-cluster lists
   const uint8_t* mk = mask + (size_t(h) * Cq + c) * Ck;
   int nsel = 0, nkeys = 0, ncomp = 0;
-  for (int b = 0; b < Ck; b += 256) {
+  for (int b = 0; b < Ck; b += 64 * NW) {
     const int i = b + tid;
     int n = 0, is_sel = 0, is_comp = 0;
     if (i < Ck) {
@@ -222,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
     }
     if (is_comp) {
       comp_s[ncomp + e3] = i;
-      cbias_s[ncomp + e3] = __log2f(float(n));
+      cbias_s[ncomp + e3] = __log2f(float(n)) / sl2;  // raw logit units
     }
     nsel += t1; nkeys += t2; ncomp += t3;
   }
@@ -236,48 +288,50 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
   const int nt_exact = (nkeys + kAttBK - 1) / kAttBK;
   const int nt_all = nt_exact + (ncomp + kAttBK - 1) / kAttBK;
 
-  // ---- asynchronous tile loads: lane `lane` of instruction i fills LDS slot
-  // (w*NI + i)*64 + lane, i.e. row slot/CPR, swizzled piece slot%CPR.
-  int cur[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) cur[i] = 0;
+  // ---- asynchronous tile loads. Lane x of every wave finds the source row
+  // of tile row x (a cursor into the selected list, advanced monotonically);
+  // each copy lane fetches the source of the row its piece slot belongs to
+  // with a shuffle. Filler rows read row 0 (finite data, weight exactly 0).
+  // The row biases are kept in raw logit units (divided by the log2 scale)
+  // so that they can seed the S accumulators.
+  int cur = 0;
   auto issue = [&](int tile, T* kd0, T* vd0, float* bd) {
     const bool exact = tile < nt_exact;  // uniform over the block
+    int src = 0;
+    float bias = -__builtin_inff();
+    if (exact) {
+      const int p = tile * kAttBK + lane;
+      if (p < nkeys) {
+        while (cur + 1 < nsel && pref_s[cur + 1] <= p) ++cur;
+        src = start_s[cur] + p;
+        bias = 0.f;
+      }
+    } else {
+      const int p = (tile - nt_exact) * kAttBK + lane;
+      if (p < ncomp) {
+        src = comp_s[p];
+        bias = cbias_s[p];
+      }
+    }
+    if (w == 0) bd[lane] = bias;
     const T* kbase = exact ? Kh : KCh;
     const T* vbase = exact ? Vh : VCh;
-    int offs[NI];  // element offset of this lane's piece in every load
+    int koffs[NI], voffs[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int slot = (w * NI + i) * 64 + lane;
-      const int row = slot / CPR, pos = slot % CPR;
-      const int piece = pos ^ swz<CPR>(row);
-      int src = 0;  // filler row 0: finite data whose weight is exactly 0
-      float bias = -__builtin_inff();
-      if (exact) {
-        const int p = tile * kAttBK + row;
-        if (p < nkeys) {
-          int cu = cur[i];
-          while (cu + 1 < nsel && pref_s[cu + 1] <= p) ++cu;
-          cur[i] = cu;
-          src = start_s[cu] + p;
-          bias = 0.f;
-        }
-      } else {
-        const int p = (tile - nt_exact) * kAttBK + row;
-        if (p < ncomp) {
-          src = comp_s[p];
-          bias = cbias_s[p];
-        }
-      }
-      offs[i] = src * D + piece * EPT;
-      if (pos == 0) bd[row] = bias;
+      const int j = (w * NI + i) * 64 + lane;
+      int row, piece;
+      L::k_slot(j, row, piece);
+      koffs[i] = __shfl(src, row, 64) * D + piece * EPT;
+      L::v_slot(j, row, piece);
+      voffs[i] = __shfl(src, row, 64) * D + piece * EPT;
     }
-    // all LDS traffic of this step is above: nothing below touches LDS
+    // all LDS traffic of this call is above: nothing below touches LDS
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kbase + offs[i]),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kbase + koffs[i]),
                                        (lds_void*)(kd0 + (w * NI + i) * 64 * EPT), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vbase + offs[i]),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vbase + voffs[i]),
                                        (lds_void*)(vd0 + (w * NI + i) * 64 * EPT), 16, 0, 0);
     }
   };
@@ -300,86 +354,107 @@ __global__ __launch_bounds__(256, 2) void attend_kernel(
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[QB], lsum[QB];
+  const float inv_sl2 = 1.f / sl2;
+  // running maximum (log2 units), its rescale threshold in raw logit units,
+  // and the running denominator of every query of this lane
+  float mrow[QB], thr[QB], lsum[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { mrow[qb] = -__builtin_inff(); lsum[qb] = 0.f; }
+  for (int qb = 0; qb < QB; ++qb) {
+    mrow[qb] = -__builtin_inff();
+    thr[qb] = -__builtin_inff();
+    lsum[qb] = 0.f;
+  }
+
+  // ---- the pieces of one 32-key half (keys 32*kh .. 32*kh+31 of a tile)
+  auto kfrags = [&](Frag<T> (&ka)[2][KC], const T* kb_s, int kh) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int k = 0; k < KC; ++k) ka[kb][k] = L::k_frag(kb_s, kh * 2 + kb, k, lane);
+  };
+  auto vfrags = [&](Frag<T> (&va)[DB], const T* vb_s, int kh) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va[db] = L::vt_frag(vb_s, kh, db, lane);
+  };
+  // S^T in raw logit units, accumulators seeded with the rows' biases
+  auto qk = [&](f32x4 (&s)[2][QB], const Frag<T> (&ka)[2][KC], const float* bb_s, int kh) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(bb_s + kh * 32 + kb * 16 + g * 4);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = b4;
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) mma(s[kb][qb], ka[kb][k], qf[qb][k]);
+  };
+  // raise the running maxima if a logit of this half exceeds its threshold;
+  // earlier O and l are scaled down to the new maximum
+  auto check = [&](const f32x4 (&s)[2][QB]) {
+    float mx[QB];
+    bool up = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = s[0][qb][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) m = fmaxf(m, s[e >> 2][qb][e & 3]);
+      mx[qb] = m;
+      up = up || (mx[qb] > thr[qb]);
+    }
+    if (__ballot(up) != 0ull) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mn = fmaxf(mrow[qb], quad_max(mx[qb]) * sl2);  // the scale is positive
+        const float a = (mn > mrow[qb]) ? fast_exp2(mrow[qb] - mn) : 1.f;
+        mrow[qb] = mn;
+        thr[qb] = (mn + kRescaleSlack) * inv_sl2;
+        lsum[qb] *= a;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db][qb] *= a;
+      }
+    }
+  };
+  // P^T fragments and their sums (the denominator adds the same rounded
+  // weights the numerator uses)
+  auto weights = [&](const f32x4 (&s)[2][QB], Frag<T> (&pb)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float nm = -mrow[qb];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pb[qb].v[e] = from_f32<T>(fast_exp2(fmaf(s[e >> 2][qb][e & 3], sl2, nm)));
+      lsum[qb] = frag_sum(pb[qb], lsum[qb]);
+    }
+  };
+  auto pv = [&](const Frag<T> (&va)[DB], const Frag<T> (&pb)[QB]) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mma(o[db][qb], va[db], pb[qb]);
+  };
 
   // one tile: start filling the other buffer with tile+1, compute this one
   auto step = [&](int tile, const T* kb_s, const T* vb_s, const float* bb_s, T* kn_s, T* vn_s,
                   float* bn_s) {
     if (tile + 1 < nt_all) issue(tile + 1, kn_s, vn_s, bn_s);
     if (active) {
-      // the 64-key tile is processed as two 32-key halves to bound registers
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        // ---- S^T = K Q^T for keys 32*kh .. 32*kh+31
-        f32x4 s[2][QB];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < KC; ++k) {
-            const Frag<T> a = load_k<D>(kb_s, kh * 32 + kb * 16 + r, k, g);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) mma(s[kb][qb], a, qf[qb][k]);
-          }
-        }
-        // ---- logits (base 2) and maxima per query
-        float bias4[2][4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) bias4[kb][i] = bb_s[kh * 32 + kb * 16 + g * 4 + i];
-        bool need = false;
-        float tmax[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float mx = -__builtin_inff();
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float v = fmaf(s[kb][qb][i], sl2, bias4[kb][i]);
-              s[kb][qb][i] = v;
-              mx = fmaxf(mx, v);
-            }
-          mx = quad_max(mx);
-          tmax[qb] = mx;
-          need = need || (mx > mrow[qb] + kRescaleSlack);
-        }
-        if (__ballot(need) != 0ull) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const float mn = (tmax[qb] > mrow[qb] + kRescaleSlack) ? tmax[qb] : mrow[qb];
-            const float al = fast_exp2(mrow[qb] - mn);
-            mrow[qb] = mn;
-            lsum[qb] *= al;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) o[db][qb] *= al;
-          }
-        }
-        // ---- P^T fragments straight from the accumulators
-        Frag<T> pb[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float ls = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = fast_exp2(s[e >> 2][qb][e & 3] - mrow[qb]);
-            ls += p;
-            pb[qb].v[e] = from_f32<T>(p);
-          }
-          lsum[qb] += ls;
-        }
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const Frag<T> va = load_vt<D>(vb_s, kh, db, r, g);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) mma(o[db][qb], va, pb[qb]);
-        }
-      }
+      Frag<T> ka0[2][KC], ka1[2][KC], va0[DB], va1[DB], pb0[QB], pb1[QB];
+      f32x4 s0[2][QB], s1[2][QB];
+      kfrags(ka0, kb_s, 0);
+      kfrags(ka1, kb_s, 1);
+      qk(s0, ka0, bb_s, 0);
+      check(s0);
+      vfrags(va0, vb_s, 0);
+      qk(s1, ka1, bb_s, 1);
+      weights(s0, pb0);
+      check(s1);
+      vfrags(va1, vb_s, 1);
+      pv(va0, pb0);
+      weights(s1, pb1);
+      pv(va1, pb1);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -431,13 +506,15 @@ static void attend_t(int H, int Nq, int Nk, int Cq, int Ck, float sl2, const voi
                      const void* Kp, const void* Vp, const int32_t* qoff, const int32_t* koff,
                      const void* kc, const void* vc, const uint8_t* mask, void* Op,
                      hipStream_t s) {
-  constexpr int BM = 64 * AttCfg<T>::QB;
-  const int grid_x = ceil_div(Nq, BM) + Cq;
+  constexpr int BM = 16 * AttCfg<T>::NW * AttCfg<T>::QB;
+  const int per_head = ceil_div(Nq, BM) + Cq;  // upper bound on query tiles per head
+  const int span = ceil_div(H * per_head, kXcds);
   const size_t lds_lists = sizeof(int) * (5 * size_t(Ck) + 1);
-  hipLaunchKernelGGL((attend_kernel<T, D>), dim3(grid_x, H), dim3(256), lds_lists, s,
+  hipLaunchKernelGGL((attend_kernel<T, D>), dim3(span * kXcds), dim3(64 * AttCfg<T>::NW), lds_lists, s,
                      static_cast<const T*>(Qp), static_cast<const T*>(Kp),
                      static_cast<const T*>(Vp), qoff, koff, static_cast<const T*>(kc),
-                     static_cast<const T*>(vc), mask, Nq, Nk, Cq, Ck, sl2, static_cast<T*>(Op));
+                     static_cast<const T*>(vc), mask, H, Nq, Nk, Cq, Ck, sl2, per_head, span,
+                     static_cast<T*>(Op));
 }
 
 hipError_t launch_attend(int elem_bytes, int H, int Nq, int Nk, int d, int Cq, int Ck,

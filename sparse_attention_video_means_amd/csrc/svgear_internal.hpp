@@ -13,6 +13,7 @@ constexpr int kChunk = 1024;      // rows per segment-sum chunk
 constexpr int kProbeUnit = 256;   // keys per probe work unit
 constexpr int kProbeGroup = 128;  // query centroids per probe block
 constexpr int kMaxClusters = 1024;
+constexpr int kXcds = 8;          // accelerator complex dies of an MI355X
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
