@@ -34,7 +34,29 @@ def parse():
     ap.add_argument("--workload", default="wan22")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run one plain device copy of COPY_BYTES "
+                         "(reference kernel for scaling memory counters)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30   # size of the --calibrate-copy copy (read once, written once)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_wan22_traffic.json")
+ATTEND_SRC = os.path.join(ROOT, "sparse_attention_video_means_amd", "csrc", "svgear_attend.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when the kernel source or the workload differs from the profiled one."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(ATTEND_SRC, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def algorithmic_flops(ra, d):
@@ -162,6 +184,14 @@ def main():
         extra["north_star_over_dense"] = north_star_ms / extra["dense_ms"]
         print(f"[bench] dense comparators: {extra}", file=sys.stderr, flush=True)
 
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)  # one elementwise kernel: COPY_BYTES read, COPY_BYTES written
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on head 0", file=sys.stderr, flush=True)
@@ -191,7 +221,8 @@ def main():
                    "exact_tflop": exact / 1e12, "compensation_tflop": comp / 1e12},
         "roofline": {"kernel": "attend_kernel<bf16,128>", "bound": "mfma",
                      "achieved": att_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": att_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": att_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(wl.name)},
         "cpu_baseline": cpu,
         **({"dense": extra} if extra else {}),
     }
