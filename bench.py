@@ -161,7 +161,7 @@ def main():
     t_att = stages["attend"] * 1e-3
     att_tflops = (exact + comp) / t_att / 1e12
     exec_tflops = exact / t_att / 1e12
-    north_star_ms = stages["cluster_q"] + stages["cluster_k"] + stages["probe"] + \
+    core_ms = stages["cluster_q"] + stages["cluster_k"] + stages["probe"] + \
         stages["route"] + stages["attend"]
 
     extra = {}
@@ -181,7 +181,7 @@ def main():
         extra["own_density1_ms"] = a.elapsed_time(b)
         dense = [x for x in (extra.get("torch_sdpa_ms"), extra["own_density1_ms"]) if x]
         extra["dense_ms"] = min(dense)
-        extra["north_star_over_dense"] = north_star_ms / extra["dense_ms"]
+        extra["core_over_dense"] = core_ms / extra["dense_ms"]
         print(f"[bench] dense comparators: {extra}", file=sys.stderr, flush=True)
 
     if args.calibrate_copy:
@@ -214,7 +214,7 @@ def main():
                                f"Cq={wl.cq} Ck={wl.ck} rho={wl.rho} iters={wl.iters}",
                    "heads": wl.heads, "n": wl.n, "d": wl.d, "cq": wl.cq, "ck": wl.ck,
                    "rho": wl.rho, "iters": wl.iters, "budget_keys": wl.budget},
-        "north_star_ms_per_head_layer": north_star_ms / wl.heads,
+        "core_ms_per_head_layer": core_ms / wl.heads,
         "stages_ms": stages,
         "attend": {"executed_block_tflops": exec_tflops,
                    "executed_block_frac_of_peak": exec_tflops / PEAK_BF16_TFLOPS,
