@@ -14,17 +14,17 @@
 //                    the S^T accumulators)
 // so P never leaves registers.
 //
-// LDS layout. Tiles are double-buffered and filled by global_load_lds_dwordx4,
-// which puts lane l's 16-byte piece at (LDS pointer + 16 l) while its global
-// address is free. The copy therefore writes every piece where the matrix
-// operands will read it: for bf16, K in MFMA fragment order (one 1 KB
-// fragment per 16 keys x 32 dims, lane order) and V in the order of the
-// transposing read ds_read_b64_tr_b16 (512 contiguous bytes per read), so
-// every LDS read of the inner loop is one contiguous, conflict-free block.
-// (f32 tiles, the reference-precision path, use plain row-major rows with
-// XOR-swizzled 16-byte pieces.) The loads of tile t+1 are issued before tile
-// t is computed; one wait and one barrier per tile. The source row of each
-// key of a tile is looked up once per lane and shared with a lane shuffle.
+// LDS layout. Tiles are filled by global_load_lds_dwordx4, which puts lane
+// l's 16-byte piece at (LDS pointer + 16 l) while its global address is free.
+// The copy therefore writes every piece where the matrix operands will read
+// it: for bf16, K in MFMA fragment order (one 1 KB fragment per 16 keys x 32
+// dims, lane order) and V in the order of the transposing read
+// ds_read_b64_tr_b16 (512 contiguous bytes per read), so every LDS read of the
+// inner loop is one contiguous, conflict-free block. (f32 tiles, the
+// reference-precision path, use plain row-major rows with XOR-swizzled
+// 16-byte pieces.) The source rows of the packed keys are tabulated in LDS
+// once per block (a window of positions at a time), so a copy lane finds its
+// row's source with one LDS read.
 //
 // Softmax. Exponentials are base 2 with log2(e) folded into the scale. The
 // row biases (0 for exact keys, ln|k_c'| for centroid rows, -inf for filler)
@@ -55,11 +55,13 @@ template <>
 struct AttCfg<__bf16> {
   static constexpr int QB = 2;              // 16-query blocks per wavefront
   static constexpr int NW = SVGEAR_ATT_NW;  // wavefronts per block
+  static constexpr int ROWS = 8192;         // packed key positions per source-row window
 };
 template <>
 struct AttCfg<float> {
   static constexpr int QB = 1;
   static constexpr int NW = 4;
+  static constexpr int ROWS = 1024;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -219,6 +221,8 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   int* comp_s = lists + 2 * Ck;        // compensated (skipped, non-empty) key clusters
   float* cbias_s = reinterpret_cast<float*>(lists + 3 * Ck);  // ln |k_c'| / scale of those
   int* pref_s = lists + 4 * Ck;        // packed offset of every selected cluster (+ total)
+  // source row of every packed exact key position in [rbase, rbase + ROWS)
+  __shared__ int rows_s[AttCfg<T>::ROWS];
   __shared__ int scratch[16];
   __shared__ int info[2];
 
@@ -288,51 +292,67 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   const int nt_exact = (nkeys + kAttBK - 1) / kAttBK;
   const int nt_all = nt_exact + (ncomp + kAttBK - 1) / kAttBK;
 
-  // ---- asynchronous tile loads. Lane x of every wave finds the source row
-  // of tile row x (a cursor into the selected list, advanced monotonically);
-  // each copy lane fetches the source of the row its piece slot belongs to
-  // with a shuffle. Filler rows read row 0 (finite data, weight exactly 0).
-  // The row biases are kept in raw logit units (divided by the log2 scale)
-  // so that they can seed the S accumulators.
-  int cur = 0;
-  auto issue = [&](int tile, T* kd0, T* vd0, float* bd) {
+  // ---- source rows of the packed exact keys, one window of ROWS positions at
+  // a time: wave w walks selected clusters w, w + NW, ... and its lanes write
+  // consecutive positions (the keys of a selected cluster are consecutive rows
+  // of the permuted tensors)
+  constexpr int ROWS = AttCfg<T>::ROWS;
+  static_assert(ROWS % kAttBK == 0, "windows hold whole tiles");
+  int rbase = 0;
+  auto fill_rows = [&](int base) {
+    for (int j = w; j < nsel; j += NW) {
+      const int a = max(pref_s[j], base), b = min(pref_s[j + 1], base + ROWS);
+      const int st = start_s[j];
+      for (int p = a + lane; p < b; p += 64) rows_s[p - base] = st + p;
+    }
+  };
+  fill_rows(0);
+  __syncthreads();
+
+  // ---- asynchronous tile loads. The tile row and 16-byte piece behind every
+  // copy lane's slot are fixed for the whole loop; per tile a lane only looks
+  // up its rows' sources (filler rows read row 0: finite data whose weight is
+  // exactly 0). The row biases are kept in raw logit units (divided by the
+  // log2 scale) so that they can seed the S accumulators.
+  int krow[NI], kpc[NI], vrow[NI], vpc[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int j = (w * NI + i) * 64 + lane;
+    L::k_slot(j, krow[i], kpc[i]);
+    L::v_slot(j, vrow[i], vpc[i]);
+  }
+  // sources of this lane's K and V rows of `tile`, its row bias, and the copies
+  auto issue = [&](int tile, T* kd, T* vd, float* bd) {
     const bool exact = tile < nt_exact;  // uniform over the block
-    int src = 0;
-    float bias = -__builtin_inff();
+    int ksrc[NI], vsrc[NI];
+    float bias;
     if (exact) {
-      const int p = tile * kAttBK + lane;
-      if (p < nkeys) {
-        while (cur + 1 < nsel && pref_s[cur + 1] <= p) ++cur;
-        src = start_s[cur] + p;
-        bias = 0.f;
+      const int p0 = tile * kAttBK;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        ksrc[i] = (p0 + krow[i] < nkeys) ? rows_s[p0 - rbase + krow[i]] : 0;
+        vsrc[i] = (p0 + vrow[i] < nkeys) ? rows_s[p0 - rbase + vrow[i]] : 0;
       }
+      bias = (p0 + lane < nkeys) ? 0.f : -__builtin_inff();
     } else {
-      const int p = (tile - nt_exact) * kAttBK + lane;
-      if (p < ncomp) {
-        src = comp_s[p];
-        bias = cbias_s[p];
+      const int p0 = (tile - nt_exact) * kAttBK;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        ksrc[i] = (p0 + krow[i] < ncomp) ? comp_s[p0 + krow[i]] : 0;
+        vsrc[i] = (p0 + vrow[i] < ncomp) ? comp_s[p0 + vrow[i]] : 0;
       }
+      bias = (p0 + lane < ncomp) ? cbias_s[p0 + lane] : -__builtin_inff();
     }
     if (w == 0) bd[lane] = bias;
     const T* kbase = exact ? Kh : KCh;
     const T* vbase = exact ? Vh : VCh;
-    int koffs[NI], voffs[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int j = (w * NI + i) * 64 + lane;
-      int row, piece;
-      L::k_slot(j, row, piece);
-      koffs[i] = __shfl(src, row, 64) * D + piece * EPT;
-      L::v_slot(j, row, piece);
-      voffs[i] = __shfl(src, row, 64) * D + piece * EPT;
-    }
     // all LDS traffic of this call is above: nothing below touches LDS
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kbase + koffs[i]),
-                                       (lds_void*)(kd0 + (w * NI + i) * 64 * EPT), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vbase + voffs[i]),
-                                       (lds_void*)(vd0 + (w * NI + i) * 64 * EPT), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kbase + ksrc[i] * D + kpc[i] * EPT),
+                                       (lds_void*)(kd + (w * NI + i) * 64 * EPT), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vbase + vsrc[i] * D + vpc[i] * EPT),
+                                       (lds_void*)(vd + (w * NI + i) * 64 * EPT), 16, 0, 0);
     }
   };
 
@@ -365,7 +385,7 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
     lsum[qb] = 0.f;
   }
 
-  // ---- the pieces of one 32-key half (keys 32*kh .. 32*kh+31 of a tile)
+  // ---- the pieces of one 32-key half kh (keys 32 kh .. 32 kh + 31 of a tile)
   auto kfrags = [&](Frag<T> (&ka)[2][KC], const T* kb_s, int kh) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -377,55 +397,55 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
     for (int db = 0; db < DB; ++db) va[db] = L::vt_frag(vb_s, kh, db, lane);
   };
   // S^T in raw logit units, accumulators seeded with the rows' biases
-  auto qk = [&](f32x4 (&s)[2][QB], const Frag<T> (&ka)[2][KC], const float* bb_s, int kh) {
+  auto qk = [&](f32x4 (&sh)[2][QB], const Frag<T> (&ka)[2][KC], const float* bb_s, int kh) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const f32x4 b4 = *reinterpret_cast<const f32x4*>(bb_s + kh * 32 + kb * 16 + g * 4);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = b4;
+      for (int qb = 0; qb < QB; ++qb) sh[kb][qb] = b4;
     }
 #pragma unroll
     for (int k = 0; k < KC; ++k)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mma(s[kb][qb], ka[kb][k], qf[qb][k]);
+        for (int qb = 0; qb < QB; ++qb) mma(sh[kb][qb], ka[kb][k], qf[qb][k]);
   };
-  // raise the running maxima if a logit of this half exceeds its threshold;
+  // raise the running maxima if a logit of the half exceeds its threshold;
   // earlier O and l are scaled down to the new maximum
-  auto check = [&](const f32x4 (&s)[2][QB]) {
+  auto check = [&](const f32x4 (&sh)[2][QB]) {
     float mx[QB];
     bool up = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float m = s[0][qb][0];
+      float m = sh[0][qb][0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) m = fmaxf(m, s[e >> 2][qb][e & 3]);
+      for (int e = 1; e < 8; ++e) m = fmaxf(m, sh[e >> 2][qb][e & 3]);
       mx[qb] = m;
-      up = up || (mx[qb] > thr[qb]);
+      up = up || (m > thr[qb]);
     }
     if (__ballot(up) != 0ull) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float mn = fmaxf(mrow[qb], quad_max(mx[qb]) * sl2);  // the scale is positive
-        const float a = (mn > mrow[qb]) ? fast_exp2(mrow[qb] - mn) : 1.f;
+        const float al = (mn > mrow[qb]) ? fast_exp2(mrow[qb] - mn) : 1.f;
         mrow[qb] = mn;
         thr[qb] = (mn + kRescaleSlack) * inv_sl2;
-        lsum[qb] *= a;
+        lsum[qb] *= al;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) o[db][qb] *= a;
+        for (int db = 0; db < DB; ++db) o[db][qb] *= al;
       }
     }
   };
   // P^T fragments and their sums (the denominator adds the same rounded
   // weights the numerator uses)
-  auto weights = [&](const f32x4 (&s)[2][QB], Frag<T> (&pb)[QB]) {
+  auto weights = [&](const f32x4 (&sh)[2][QB], Frag<T> (&pb)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float nm = -mrow[qb];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        pb[qb].v[e] = from_f32<T>(fast_exp2(fmaf(s[e >> 2][qb][e & 3], sl2, nm)));
+        pb[qb].v[e] = from_f32<T>(fast_exp2(fmaf(sh[e >> 2][qb][e & 3], sl2, nm)));
       lsum[qb] = frag_sum(pb[qb], lsum[qb]);
     }
   };
@@ -439,6 +459,13 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   // one tile: start filling the other buffer with tile+1, compute this one
   auto step = [&](int tile, const T* kb_s, const T* vb_s, const float* bb_s, T* kn_s, T* vn_s,
                   float* bn_s) {
+    if (tile + 1 < nt_exact && (tile + 1) * kAttBK == rbase + ROWS) {
+      // the next tile starts a new window of source rows (every wave is past
+      // its reads of the current window: the last barrier)
+      rbase += ROWS;
+      fill_rows(rbase);
+      __syncthreads();
+    }
     if (tile + 1 < nt_all) issue(tile + 1, kn_s, vn_s, bn_s);
     if (active) {
       Frag<T> ka0[2][KC], ka1[2][KC], va0[DB], va1[DB], pb0[QB], pb1[QB];
