@@ -412,8 +412,10 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
         for (int qb = 0; qb < QB; ++qb) mma(sh[kb][qb], ka[kb][k], qf[qb][k]);
   };
   // raise the running maxima if a logit of the half exceeds its threshold;
-  // earlier O and l are scaled down to the new maximum
-  auto check = [&](const f32x4 (&sh)[2][QB]) {
+  // l is scaled down to the new maximum at once and the factors are returned
+  // for O (true if any is not 1), which the caller scales once every weight
+  // computed under the old maxima has been added to it
+  auto check = [&](const f32x4 (&sh)[2][QB], float (&al)[QB]) -> bool {
     float mx[QB];
     bool up = false;
 #pragma unroll
@@ -424,18 +426,22 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
       mx[qb] = m;
       up = up || (m > thr[qb]);
     }
-    if (__ballot(up) != 0ull) {
+    if (__ballot(up) == 0ull) return false;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mn = fmaxf(mrow[qb], quad_max(mx[qb]) * sl2);  // the scale is positive
-        const float al = (mn > mrow[qb]) ? fast_exp2(mrow[qb] - mn) : 1.f;
-        mrow[qb] = mn;
-        thr[qb] = (mn + kRescaleSlack) * inv_sl2;
-        lsum[qb] *= al;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db][qb] *= al;
-      }
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mn = fmaxf(mrow[qb], quad_max(mx[qb]) * sl2);  // the scale is positive
+      al[qb] = (mn > mrow[qb]) ? fast_exp2(mrow[qb] - mn) : 1.f;
+      mrow[qb] = mn;
+      thr[qb] = (mn + kRescaleSlack) * inv_sl2;
+      lsum[qb] *= al[qb];
     }
+    return true;
+  };
+  auto scale_o = [&](const float (&al)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db][qb] *= al[qb];
   };
   // P^T fragments and their sums (the denominator adds the same rounded
   // weights the numerator uses)
@@ -472,15 +478,17 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
       f32x4 s0[2][QB], s1[2][QB];
       kfrags(ka0, kb_s, 0);
       kfrags(ka1, kb_s, 1);
+      float al0[QB], al1[QB];
       qk(s0, ka0, bb_s, 0);
-      check(s0);
+      if (check(s0, al0)) scale_o(al0);
       vfrags(va0, vb_s, 0);
       qk(s1, ka1, bb_s, 1);
       weights(s0, pb0);
-      check(s1);
+      const bool up1 = check(s1, al1);
       vfrags(va1, vb_s, 1);
-      pv(va0, pb0);
+      pv(va0, pb0);             // weights of the old maxima first,
       weights(s1, pb1);
+      if (up1) scale_o(al1);    // then O follows l to the new maxima
       pv(va1, pb1);
     }
     __builtin_amdgcn_s_waitcnt(0);

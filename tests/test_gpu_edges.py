@@ -195,3 +195,30 @@ def test_cluster_extreme_counts(n, d, c, dtype):
     means = O.segment_means(x[np.argsort(lab, kind="stable")],
                             np.concatenate([[0], np.cumsum(np.bincount(lab, minlength=c))]))
     np.testing.assert_allclose(mu[nz], means[nz], rtol=2e-6, atol=2e-6)
+
+
+def test_running_maximum_jumps_inside_a_tile():
+    """Logits that rise by far more than the kernel's rescale slack from one
+    32-key half of a tile to the next (and from tile to tile): every jump
+    forces the running maximum up while earlier weights are still being
+    accumulated, in the same order the kernel walks the keys."""
+    n, d = 320, 128
+    rng = np.random.default_rng(20)
+    step = np.repeat(np.arange(n // 32), 32).astype(np.float32)        # +1 every 32 keys
+    k = np.zeros((1, n, d), np.float32)
+    k[0, :, 0] = 4.0 * step                                            # q.k rises 4*40*tau per half
+    k[0, :, 1:] = 0.1 * rng.standard_normal((n, d - 1))
+    q = np.zeros((1, 96, d), np.float32)
+    q[0, :, 0] = 40.0
+    q[0, :, 1:] = 0.1 * rng.standard_normal((96, d - 1))
+    v = rng.standard_normal((1, n, d)).astype(np.float32)
+    to = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    zq, zk = np.zeros((1, 96), np.int32), np.zeros((1, n), np.int32)
+    # one key cluster, fully selected: the exact tiles walk the keys in order
+    res = check_path(to(q), to(k), to(v), zq, zk, 1, 1, budget=n)
+    assert int(res["sel_count"].sum()) == 1
+    # two key clusters, the rising one skipped: its centroid term is the
+    # largest logit and arrives after the exact tiles
+    lk = (np.arange(n) >= 64).astype(np.int32)[None]
+    res = check_path(to(q), to(k), to(v), zq, lk, 1, 2, budget=64)
+    assert int(res["sel_mask"][0, 0, 0]) == 1 and int(res["sel_mask"][0, 0, 1]) == 0
