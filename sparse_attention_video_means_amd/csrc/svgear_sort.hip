@@ -150,7 +150,11 @@ __global__ __launch_bounds__(256) void segsum_kernel(int N, int C, int nt, int m
   constexpr int TPR = D / EPT;              // threads per row
   constexpr int RPI = 256 / TPR;            // rows per iteration
   __shared__ float red[RPI][D];
-  const int h = blockIdx.y, q = blockIdx.x, tid = threadIdx.x;
+  // heads in reverse launch order: the assignment pass before this one walked
+  // them forwards, so the rows it read last are the ones still in the
+  // last-level cache when this pass starts (and the next assignment, walking
+  // forwards again, starts on what this pass read last)
+  const int h = int(gridDim.y) - 1 - int(blockIdx.y), q = blockIdx.x, tid = threadIdx.x;
   const int32_t* cp = chunk_prefix + size_t(h) * (C + 1);
   if (q >= cp[C]) return;
   const int c = find_segment(cp, C, q);
@@ -158,27 +162,32 @@ __global__ __launch_bounds__(256) void segsum_kernel(int N, int C, int nt, int m
   const int p0 = off[c] + (q - cp[c]) * kChunk;
   const int p1 = min(off[c + 1], p0 + kChunk);
   const int rg = tid / TPR, col = tid % TPR;
+  // the chunk's source rows, read once (coalesced) for every tensor
+  __shared__ int prow[kChunk];
+  const int len = p1 - p0;
+  for (int i = tid; i < len; i += 256) prow[i] = perm[size_t(h) * N + p0 + i];
+  __syncthreads();
   for (int k = 0; k < nt; ++k) {
     const T* s = static_cast<const T*>(src.p[k]) + size_t(h) * N * D;
     T* dd = dst.p[k] ? static_cast<T*>(dst.p[k]) + size_t(h) * N * D : nullptr;
     float acc[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
-    // four rows in flight per thread; rows are still added in slot order
-    constexpr int U = 4;
-    for (int p = p0 + rg; p < p1; p += U * RPI) {
-      int row[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) row[u] = (p + u * RPI < p1) ? perm[size_t(h) * N + p + u * RPI] : -1;
+    // eight rows in flight per thread; rows are still added in slot order
+    constexpr int U = 8;
+    for (int j = rg; j < len; j += U * RPI) {
       uint4 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        v[u] = row[u] >= 0 ? *reinterpret_cast<const uint4*>(s + size_t(row[u]) * D + col * EPT)
-                           : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < U; ++u) {
+        const int jj = j + u * RPI;
+        v[u] = jj < len ? *reinterpret_cast<const uint4*>(s + size_t(prow[jj]) * D + col * EPT)
+                        : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (row[u] < 0) break;
-        if (dd) *reinterpret_cast<uint4*>(dd + size_t(p + u * RPI) * D + col * EPT) = v[u];
+        const int jj = j + u * RPI;
+        if (jj >= len) break;
+        if (dd) *reinterpret_cast<uint4*>(dd + size_t(p0 + jj) * D + col * EPT) = v[u];
         const T* el = reinterpret_cast<const T*>(&v[u]);
 #pragma unroll
         for (int e = 0; e < EPT; ++e) acc[e] += to_f32(el[e]);
