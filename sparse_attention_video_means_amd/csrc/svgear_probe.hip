@@ -116,21 +116,47 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
 
   const T* Kh = Kp + size_t(h) * Nk * D;
   const int srow = tid >> 2, sq = tid & 3;
+  constexpr int RAW = QD * int(sizeof(T)) / 16;  // 16-byte loads per thread and tile
 
-  for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
-    const int cc = find_unit_cluster(up, Ck, u);
-    const int j0 = ko[cc] + (u - up[cc]) * kProbeUnit;
-    const int j1 = min(ko[cc + 1], j0 + kProbeUnit);
-    float kb[QD];  // this thread's quarter of the key centroid row
-    {
-      const float* kr = kc + (size_t(h) * Ck + cc) * D + sq * QD;
+  // The block walks its units u = blockIdx.x, +gridDim.x, ... and each unit
+  // in 64-key tiles. The raw key rows (and, at a unit's first tile, the key
+  // centroid) of the next tile are loaded into registers while the current
+  // tile is multiplied, so their latency is off the critical path.
+  struct Tile {
+    int u, cc, j0, j1, tj;
+  };
+  auto unit_tile = [&](int u) {
+    Tile t;
+    t.u = u;
+    t.cc = find_unit_cluster(up, Ck, u);
+    t.j0 = ko[t.cc] + (u - up[t.cc]) * kProbeUnit;
+    t.j1 = min(ko[t.cc + 1], t.j0 + kProbeUnit);
+    t.tj = t.j0;
+    return t;
+  };
+  auto load_raw = [&](const Tile& t, uint4 (&raw)[RAW]) {
+    const bool ok = t.tj + srow < t.j1;
+    const T* src = Kh + size_t(ok ? t.tj + srow : 0) * D + sq * QD;
 #pragma unroll
-      for (int i = 0; i < QD; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(kr + i);
-        kb[i] = v.x; kb[i + 1] = v.y; kb[i + 2] = v.z; kb[i + 3] = v.w;
-      }
+    for (int i = 0; i < RAW; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+  };
+  auto load_kbar = [&](int cc, float (&kb)[QD]) {
+    const float* kr = kc + (size_t(h) * Ck + cc) * D + sq * QD;
+#pragma unroll
+    for (int i = 0; i < QD; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(kr + i);
+      kb[i] = v.x; kb[i + 1] = v.y; kb[i + 2] = v.z; kb[i + 3] = v.w;
     }
-    float st[2], mp[2], Z[2], E[2], e2[2];
+  };
+
+  if (int(blockIdx.x) >= nunits) return;
+  Tile cur = unit_tile(blockIdx.x);
+  uint4 raw[RAW];
+  float kb[QD], kbn[QD];
+  load_raw(cur, raw);
+  load_kbar(cur.cc, kb);
+  float st[2], mp[2], Z[2], E[2], e2[2];
+  auto unit_start = [&](int cc) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       st[cb] = cok[cb] ? st2g[(size_t(h) * Cq + cidx[cb]) * Ck + cc] : 0.f;
@@ -139,98 +165,121 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
       E[cb] = 0.f;
       e2[cb] = 1.f;
     }
-    for (int tj = j0; tj < j1; tj += 64) {
-      __syncthreads();
-      {  // stage (k - kbar) as T high part + T remainder; rows past the unit are zero
-        const bool ok = tj + srow < j1;
-        const T* src = Kh + size_t(ok ? tj + srow : 0) * D + sq * QD;
-        T* dst = ks + srow * LDR + sq * QD;
-        T* dlo = kl + srow * LDR + sq * QD;
+  };
+  unit_start(cur.cc);
+
+  while (true) {
+    __syncthreads();
+    {  // stage (k - kbar) as T high part + T remainder; rows past the unit are zero
+      const bool ok = cur.tj + srow < cur.j1;
+      T* dst = ks + srow * LDR + sq * QD;
+      T* dlo = kl + srow * LDR + sq * QD;
 #pragma unroll
-        for (int i = 0; i < QD; i += 16 / sizeof(T)) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(src + i);
-          const T* el = reinterpret_cast<const T*>(&raw);
-          T out[16 / sizeof(T)], rem[16 / sizeof(T)];
+      for (int i = 0; i < RAW; ++i) {
+        const T* el = reinterpret_cast<const T*>(&raw[i]);
+        constexpr int E8 = 16 / sizeof(T);
+        T out[E8], rem[E8];
 #pragma unroll
-          for (int e = 0; e < int(16 / sizeof(T)); ++e) {
-            const float dlt = ok ? to_f32(el[e]) - kb[i + e] : 0.f;
-            out[e] = from_f32<T>(dlt);
-            rem[e] = from_f32<T>(dlt - to_f32(out[e]));
-          }
-          *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(out);
-          if (kSplit) *reinterpret_cast<uint4*>(dlo + i) = *reinterpret_cast<const uint4*>(rem);
+        for (int e = 0; e < E8; ++e) {
+          const float dlt = ok ? to_f32(el[e]) - kb[i * E8 + e] : 0.f;
+          out[e] = from_f32<T>(dlt);
+          rem[e] = from_f32<T>(dlt - to_f32(out[e]));
         }
+        *reinterpret_cast<uint4*>(dst + i * E8) = *reinterpret_cast<const uint4*>(out);
+        if (kSplit) *reinterpret_cast<uint4*>(dlo + i * E8) = *reinterpret_cast<const uint4*>(rem);
       }
-      __syncthreads();
-      const int nvalid = min(64, j1 - tj);
-      for (int kb16 = 0; kb16 * 16 < nvalid; ++kb16) {
-        Frag<T> a[KC], al[KC];
+    }
+    __syncthreads();
+    // the next tile: the rest of this unit, else the first tile of the next
+    Tile nxt = cur;
+    nxt.tj += 64;
+    const bool new_unit = nxt.tj >= cur.j1;
+    if (new_unit) {
+      const int un = cur.u + int(gridDim.x);
+      if (un < nunits) nxt = unit_tile(un);
+      else nxt.u = nunits;  // no next tile
+    }
+    const bool more = nxt.u < nunits;
+    if (more) {
+      load_raw(nxt, raw);
+      if (new_unit) load_kbar(nxt.cc, kbn);
+    }
+    const int nvalid = min(64, cur.j1 - cur.tj);
+    for (int kb16 = 0; kb16 * 16 < nvalid; ++kb16) {
+      Frag<T> a[KC], al[KC];
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        a[k] = load8(&ks[(kb16 * 16 + r) * LDR + k * 32 + g * 8]);
+        if (kSplit) al[k] = load8(&kl[(kb16 * 16 + r) * LDR + k * 32 + g * 8]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        if (!blk_live[cb]) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // (qhi + qlo).(dhi + dlo) without the qlo.dlo term (below 2^-16 relative)
 #pragma unroll
         for (int k = 0; k < KC; ++k) {
-          a[k] = load8(&ks[(kb16 * 16 + r) * LDR + k * 32 + g * 8]);
-          if (kSplit) al[k] = load8(&kl[(kb16 * 16 + r) * LDR + k * 32 + g * 8]);
+          mma(acc, a[k], bq[cb][k]);
+          if (kSplit) {
+            mma(acc, a[k], bl[cb][k]);
+            mma(acc, al[k], bq[cb][k]);
+          }
+        }
+        // lane holds delta for keys kb16*16 + 4g + i of centroid cidx[cb]
+        float d2[4];
+        float tmax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = kb16 * 16 + g * 4 + i < nvalid;
+          d2[i] = ok ? acc[i] * sl2 : -__builtin_inff();
+          tmax = fmaxf(tmax, d2[i]);
+        }
+        if (tmax > mp[cb]) {
+          const float al = fast_exp2(mp[cb] - tmax);
+          Z[cb] *= al;
+          E[cb] *= al * al;
+          mp[cb] = tmax;
+          e2[cb] = fast_exp2(-tmax);
         }
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          if (!blk_live[cb]) continue;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          // (qhi + qlo).(dhi + dlo) without the qlo.dlo term (below 2^-16 relative)
-#pragma unroll
-          for (int k = 0; k < KC; ++k) {
-            mma(acc, a[k], bq[cb][k]);
-            if (kSplit) {
-              mma(acc, a[k], bl[cb][k]);
-              mma(acc, al[k], bq[cb][k]);
-            }
-          }
-          // lane holds delta for keys kb16*16 + 4g + i of centroid cidx[cb]
-          float d2[4];
-          float tmax = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool ok = kb16 * 16 + g * 4 + i < nvalid;
-            d2[i] = ok ? acc[i] * sl2 : -__builtin_inff();
-            tmax = fmaxf(tmax, d2[i]);
-          }
-          if (tmax > mp[cb]) {
-            const float al = fast_exp2(mp[cb] - tmax);
-            Z[cb] *= al;
-            E[cb] *= al * al;
-            mp[cb] = tmax;
-            e2[cb] = fast_exp2(-tmax);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (kb16 * 16 + g * 4 + i < nvalid) {
-              const float e = fast_exp2(d2[i] - mp[cb]);
-              Z[cb] += e;
-              const float dd = e - e2[cb];
-              E[cb] = fmaf(dd, dd, E[cb]);
-            }
+        for (int i = 0; i < 4; ++i) {
+          if (kb16 * 16 + g * 4 + i < nvalid) {
+            const float e = fast_exp2(d2[i] - mp[cb]);
+            Z[cb] += e;
+            const float dd = e - e2[cb];
+            E[cb] = fmaf(dd, dd, E[cb]);
           }
         }
       }
     }
+    if (new_unit) {
+      // the unit is done: merge the four lanes of each centroid and record
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+      for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-      for (int o = 16; o <= 32; o <<= 1) {
-        const float om = __shfl_xor(mp[cb], o, 64);
-        const float oZ = __shfl_xor(Z[cb], o, 64);
-        const float oE = __shfl_xor(E[cb], o, 64);
-        const float M = fmaxf(mp[cb], om);
-        const float a1 = fast_exp2(mp[cb] - M), a2 = fast_exp2(om - M);
-        Z[cb] = Z[cb] * a1 + oZ * a2;
-        E[cb] = E[cb] * (a1 * a1) + oE * (a2 * a2);
-        mp[cb] = M;
+        for (int o = 16; o <= 32; o <<= 1) {
+          const float om = __shfl_xor(mp[cb], o, 64);
+          const float oZ = __shfl_xor(Z[cb], o, 64);
+          const float oE = __shfl_xor(E[cb], o, 64);
+          const float M = fmaxf(mp[cb], om);
+          const float a1 = fast_exp2(mp[cb] - M), a2 = fast_exp2(om - M);
+          Z[cb] = Z[cb] * a1 + oZ * a2;
+          E[cb] = E[cb] * (a1 * a1) + oE * (a2 * a2);
+          mp[cb] = M;
+        }
+        if (g == 0 && cok[cb]) {
+          float* o = rec + ((size_t(h) * maxu + cur.u) * Cq + cidx[cb]) * 3;
+          o[0] = st[cb] + mp[cb];  // absolute base-2 reference of this unit
+          o[1] = Z[cb];
+          o[2] = E[cb];
+        }
       }
-      if (g == 0 && cok[cb]) {
-        float* o = rec + ((size_t(h) * maxu + u) * Cq + cidx[cb]) * 3;
-        o[0] = st[cb] + mp[cb];  // absolute base-2 reference of this unit
-        o[1] = Z[cb];
-        o[2] = E[cb];
-      }
+      if (!more) break;
+#pragma unroll
+      for (int i = 0; i < QD; ++i) kb[i] = kbn[i];
+      unit_start(nxt.cc);
     }
+    cur = nxt;
   }
 }
 
