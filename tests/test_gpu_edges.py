@@ -222,3 +222,22 @@ def test_running_maximum_jumps_inside_a_tile():
     lk = (np.arange(n) >= 64).astype(np.int32)[None]
     res = check_path(to(q), to(k), to(v), zq, lk, 1, 2, budget=64)
     assert int(res["sel_mask"][0, 0, 0]) == 1 and int(res["sel_mask"][0, 0, 1]) == 0
+
+
+def test_selection_larger_than_a_source_row_window():
+    """More exact keys than one window of the kernel's source-row table holds
+    (8192 positions for bf16, 1024 for f32), so the table is refilled
+    mid-stream, across clusters of uneven size."""
+    rng = np.random.default_rng(21)
+    q, k, v = data(1, 20000, 128, "bf16", 21)
+    lq = rng.integers(0, 6, size=(1, 20000)).astype(np.int32)
+    sizes = rng.zipf(1.3, size=40).astype(np.float64)
+    p = sizes / sizes.sum()
+    lk = rng.choice(40, size=(1, 20000), p=p).astype(np.int32)
+    res = check_path(q, k, v, lq, lk, 6, 40, budget=12000)
+    assert int(res["sel_keys"].max()) > 8192
+    qf, kf, vf = data(1, 3000, 64, "f32", 22)
+    lqf = rng.integers(0, 3, size=(1, 3000)).astype(np.int32)
+    lkf = rng.integers(0, 9, size=(1, 3000)).astype(np.int32)
+    res = check_path(qf, kf, vf, lqf, lkf, 3, 9, budget=2500)
+    assert int(res["sel_keys"].max()) > 1024

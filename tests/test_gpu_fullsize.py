@@ -1,14 +1,16 @@
-"""Full-size parity on the Wan2.2-shaped layer (needs an MI355X).
+"""Full-size parity on the full-size layers (needs an MI355X).
 
-The whole path runs exactly as the benchmark times it: `RoutedAttention` with
-40 heads x 75,600 tokens x d=128 in bf16, C_q=100, C_k=500, density 0.10, 10
-Lloyd iterations. The oracle cannot redo a 40-head layer in seconds, so its
-checks are sampled on two heads (the first and the last):
+The whole path runs exactly as the benchmark times it (`RoutedAttention`) on
+the Wan2.2-shaped layer (40 heads x 75,600 tokens x d=128, bf16, C_q=100,
+C_k=500, density 0.10, 10 Lloyd iterations), the HunyuanVideo-shaped layer
+(24 heads x 118,800 tokens) and the routing-stress layer at C_k=1000 and
+density 0.30. The oracle cannot redo such a layer in seconds, so its checks
+are sampled on two heads (the first and the last):
   * k-means: final centroids are the means of the final labels; counts match;
   * permutation and offsets: bit-exact for the whole head; gathered rows exact;
   * probe: ratio rows of four query clusters (smallest, largest and two
-    others), against all 75,600 keys;
-  * route: bit-exact for all 100 query clusters on the GPU ratios;
+    others), against every key of the head;
+  * route: bit-exact for every query cluster on the GPU ratios;
   * attend: 16 queries (first 8 and last 8 rows) of each of three query
     clusters, against the oracle's materialised softmax rows;
   * unpermute: bit-exact for the whole head.
@@ -31,10 +33,19 @@ def f64(t):
     return t.detach().float().cpu().double().numpy()
 
 
-@pytest.fixture(scope="module")
-def layer():
+LAYERS = {
+    "wan22": synth.WORKLOADS["wan22"],
+    "hunyuan": synth.WORKLOADS["hunyuan"],
+    # routing stress at its largest cluster count and density: 22,680 exact
+    # keys per query cluster
+    "stress_ck1000_rho0.3": synth.WORKLOADS["stress"].with_(ck=1000, rho=0.3),
+}
+
+
+@pytest.fixture(scope="module", params=list(LAYERS))
+def layer(request):
     from sparse_attention_video_means_amd import svgear
-    wl = synth.WORKLOADS["wan22"]
+    wl = LAYERS[request.param]
     print(f"[fullsize] generating {wl.name}: H={wl.heads} N={wl.n}", flush=True)
     q, k, v = synth.make_qkv(wl, threads=16)
     iq = synth.kmeans_init(q, wl.cq, wl.seed, 0)
@@ -45,12 +56,15 @@ def layer():
     ra(q.cuda(), k.cuda(), v.cuda(), iq.cuda(), ik.cuda())
     torch.cuda.synchronize()
     print("[fullsize] checking", flush=True)
-    return wl, q, k, v, ra
+    yield wl, q, k, v, ra
+    del ra, q, k, v
+    torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("h", [0, 39])
-def test_wan22_sampled_parity(layer, h):
+@pytest.mark.parametrize("which", ["first", "last"])
+def test_full_layer_sampled_parity(layer, which):
     wl, q, k, v, ra = layer
+    h = 0 if which == "first" else wl.heads - 1
     scale = 1 / math.sqrt(wl.d)
     lq, lk = f64(ra.labels_q[h]), f64(ra.labels_k[h])
     # k-means: counts and final centroids
