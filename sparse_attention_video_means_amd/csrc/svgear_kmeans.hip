@@ -3,7 +3,8 @@
 //
 // Each block takes 256 rows of one head. Its four wavefronts keep their 64
 // rows as MFMA B operands in registers and stream the centroid table through
-// LDS in chunks of 64 centroids. The table already holds -2 * round(mu) in the
+// LDS in chunks of 64 centroids, fetching the next chunk into registers while
+// the current one is multiplied. The table already holds -2 * round(mu) in the
 // input element type and ||round(mu)||^2 in f32, so one chain of MFMAs seeded
 // with the norms yields ||mu||^2 - 2 x.mu directly. Each lane keeps a running
 // (distance, index) minimum over the centroids it sees in increasing index
@@ -52,17 +53,33 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X,
   const T* tabh = table + size_t(h) * C * D;
   const float* nrmh = norms + size_t(h) * C;
   constexpr int EPT = 16 / sizeof(T);
-  constexpr int CPR = D / EPT;  // 16-byte pieces per row
+  constexpr int CPR = D / EPT;                      // 16-byte pieces per row
+  constexpr int PPT = kAssignChunk * CPR / 256;     // pieces per thread per chunk
+  // The next chunk of the table is fetched into registers while the current
+  // one is multiplied, so the table's load latency is paid once per block.
+  uint4 pre[PPT];
+  float pre_nrm = 0.f;
+  auto fetch = [&](int cbase) {
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      const int i = tid + p * 256, row = i / CPR, piece = i % CPR;
+      pre[p] = (cbase + row < C)
+                   ? *reinterpret_cast<const uint4*>(tabh + size_t(cbase + row) * D + piece * EPT)
+                   : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < kAssignChunk) pre_nrm = (cbase + tid < C) ? nrmh[cbase + tid] : __builtin_inff();
+  };
+  fetch(0);
   for (int cbase = 0; cbase < C; cbase += kAssignChunk) {
     __syncthreads();
-    for (int i = tid; i < kAssignChunk * CPR; i += 256) {
-      const int row = i / CPR, piece = i % CPR;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (cbase + row < C) v = *reinterpret_cast<const uint4*>(tabh + size_t(cbase + row) * D + piece * EPT);
-      *reinterpret_cast<uint4*>(&tab[row * LDR + piece * EPT]) = v;
+#pragma unroll
+    for (int p = 0; p < PPT; ++p) {
+      const int i = tid + p * 256, row = i / CPR, piece = i % CPR;
+      *reinterpret_cast<uint4*>(&tab[row * LDR + piece * EPT]) = pre[p];
     }
-    if (tid < kAssignChunk) nrm[tid] = (cbase + tid < C) ? nrmh[cbase + tid] : __builtin_inff();
+    if (tid < kAssignChunk) nrm[tid] = pre_nrm;
     __syncthreads();
+    if (cbase + kAssignChunk < C) fetch(cbase + kAssignChunk);
     const int nblk = min(kAssignChunk, C - cbase + 15) / 16;
     for (int cb = 0; cb < nblk; ++cb) {
       Frag<T> a[KC];
