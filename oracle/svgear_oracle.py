@@ -35,7 +35,7 @@ import numpy as np
 
 __all__ = [
     "round_operand", "kmeans_assign", "kmeans_update", "kmeans", "permute", "gather",
-    "segment_means", "probe", "route", "attend", "unpermute", "dense_attention",
+    "segment_means", "probe", "route", "route_global", "attend", "unpermute", "dense_attention",
     "routed_attention_head", "RoutedResult",
 ]
 
@@ -263,6 +263,54 @@ def route(ratio, k_offsets, budget_keys: int, fill: str = "skip"):
         cnt[c] = sel.size
         used_keys[c] = used
     return mask, lst, cnt, used_keys
+
+
+def route_global(ratio, q_offsets, k_offsets, budget_entries: int, fill: str = "skip"):
+    """Greedy error-to-cost routing over every block of a head at once.
+
+    Section 4.1 bounds the number of exact entries of the block mask by
+    rho * N_q * N_k for the whole attention map, and Section 4.2 selects the
+    blocks with the highest error-to-size ratio first until that budget is
+    used. Here every block (c, c') with a non-empty query cluster c and a
+    non-empty key cluster c' competes for one head-wide budget of
+    ``budget_entries`` exact (query, key) entries, and a block costs
+    |q_c| * |k_c'| entries (Section 5's split of the budget per query cluster
+    is not applied; ``route`` applies it).
+
+    Order: ratio highest first; equal ratios lower query cluster first, then
+    lower key cluster. The walk and ``fill`` are those of ``route``.
+
+    Returns (mask [Cq, Ck] uint8, list [Cq, Ck] int32 ascending and padded with
+    -1, count [Cq] int32, keys [Cq] int32 = exact keys of each query cluster,
+    used = exact entries used, an int).
+    """
+    ratio = np.asarray(ratio, dtype=np.float64)
+    nq = np.diff(np.asarray(q_offsets)).astype(np.int64)
+    nk = np.diff(np.asarray(k_offsets)).astype(np.int64)
+    cq, ck = ratio.shape
+    cs, ks = np.meshgrid(np.arange(cq), np.arange(ck), indexing="ij")
+    live = (nq[cs] > 0) & (nk[ks] > 0)
+    c_live, k_live = cs[live], ks[live]
+    order = np.lexsort((k_live, c_live, -ratio[c_live, k_live]))
+    mask = np.zeros((cq, ck), dtype=np.uint8)
+    used = 0
+    for t in order:
+        c, j = int(c_live[t]), int(k_live[t])
+        cost = int(nq[c] * nk[j])
+        if used + cost <= budget_entries:
+            mask[c, j] = 1
+            used += cost
+        elif fill == "stop":
+            break
+    lst = np.full((cq, ck), -1, dtype=np.int32)
+    cnt = np.zeros(cq, dtype=np.int32)
+    keys = np.zeros(cq, dtype=np.int32)
+    for c in range(cq):
+        sel = np.nonzero(mask[c])[0]
+        lst[c, : sel.size] = sel
+        cnt[c] = sel.size
+        keys[c] = int(nk[sel].sum())
+    return mask, lst, cnt, keys, used
 
 
 # ----------------------------------------------------------------------------

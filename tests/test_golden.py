@@ -35,6 +35,21 @@ def test_route_worked_case(fill):
     assert int(keys[0]) == g[f"used_{fill}"]
 
 
+@pytest.mark.parametrize("fill", ["skip", "stop"])
+def test_route_global_worked_case(fill):
+    g = load("route_global.txt")
+    qo = np.concatenate([[0], np.cumsum(g["q_sizes"])]).astype(np.int64)
+    ko = np.concatenate([[0], np.cumsum(g["k_sizes"])]).astype(np.int64)
+    mask, lst, count, keys, used = O.route_global(np.asarray(g["ratios"]), qo, ko, g["budget"],
+                                                  fill=fill)
+    want = g[f"selected_{fill}"]
+    for c in range(2):
+        assert np.nonzero(mask[c])[0].tolist() == want[c]
+        assert lst[c, :count[c]].tolist() == want[c]
+    assert keys.tolist() == g[f"keys_{fill}"]
+    assert used == g[f"used_{fill}"]
+
+
 def test_probe_worked_case():
     g = load("probe_two_keys.txt")
     keys = np.asarray(g["keys"])

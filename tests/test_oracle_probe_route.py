@@ -194,3 +194,85 @@ def test_route_never_exceeds_budget_random():
             # no unselected non-empty cluster would still fit
             left = budget - keys[c]
             assert not np.any((mask[c] == 0) & (counts > 0) & (counts <= left))
+
+
+# ---------------------------------------------------------------- global route
+@pytest.mark.parametrize("seed", range(4))
+def test_route_global_one_query_cluster_is_route(seed):
+    # With one query cluster of n queries every block costs n * |k_c'|, so a
+    # head-wide budget of n * B entries selects what the per-cluster route
+    # selects with B keys.
+    rng = np.random.default_rng(40 + seed)
+    counts = rng.integers(0, 30, 40)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    ratio = rng.random((1, 40))
+    ratio[0, counts == 0] = -1
+    ratio[0, rng.integers(0, 40, 6)] = 0.5  # ties
+    n = int(rng.integers(1, 50))
+    budget = int(rng.integers(0, off[-1] + 1))
+    for fill in ("skip", "stop"):
+        m1, l1, c1, k1 = O.route(ratio, off, budget, fill=fill)
+        m2, l2, c2, k2, used = O.route_global(ratio, [0, n], off, n * budget, fill=fill)
+        np.testing.assert_array_equal(m1, m2)
+        np.testing.assert_array_equal(l1, l2)
+        np.testing.assert_array_equal(c1, c2)
+        np.testing.assert_array_equal(k1, k2)
+        assert used == n * int(k1[0])
+
+
+def test_route_global_budget_extremes_and_empty_clusters():
+    rng = np.random.default_rng(41)
+    nq = np.array([3, 0, 5, 2])
+    nk = np.array([5, 0, 7, 3, 9, 1])
+    qo = np.concatenate([[0], np.cumsum(nq)])
+    ko = np.concatenate([[0], np.cumsum(nk)])
+    ratio = rng.random((4, 6))
+    ratio[:, 1] = -1
+    mask, lst, cnt, keys, used = O.route_global(ratio, qo, ko, int(qo[-1] * ko[-1]))
+    live = (nq[:, None] > 0) & (nk[None, :] > 0)
+    np.testing.assert_array_equal(mask, live.astype(np.uint8))
+    assert used == int(qo[-1] * ko[-1])
+    np.testing.assert_array_equal(keys, np.where(nq > 0, ko[-1], 0))
+    np.testing.assert_array_equal(lst[1], [-1] * 6)
+    mask, lst, cnt, keys, used = O.route_global(ratio, qo, ko, 0)
+    assert mask.sum() == 0 and np.all(lst == -1) and used == 0 and np.all(keys == 0)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_route_global_equal_costs_is_optimal_subset(seed):
+    # Equal block costs: the greedy pick maximises the covered error
+    # (sum of ratio * cost) among all block sets that fit; enumerate them.
+    rng = np.random.default_rng(50 + seed)
+    cq, ck, a, b = 3, 4, 2, 3
+    qo, ko = np.arange(0, (cq + 1) * a, a), np.arange(0, (ck + 1) * b, b)
+    ratio = rng.random((cq, ck))
+    budget = int(rng.integers(0, cq * ck * a * b + 1))
+    mask, _, _, _, used = O.route_global(ratio, qo, ko, budget)
+    blocks = [(c, j) for c in range(cq) for j in range(ck)]
+    best = -1.0
+    for r in range(len(blocks) + 1):
+        if r * a * b > budget:
+            break
+        for sub in itertools.combinations(blocks, r):
+            best = max(best, float(sum(ratio[c, j] for c, j in sub)))
+    got = float(sum(ratio[c, j] for c, j in blocks if mask[c, j]))
+    assert got == pytest.approx(best, rel=1e-12)
+    assert used <= budget
+
+
+def test_route_global_never_exceeds_budget_random():
+    rng = np.random.default_rng(60)
+    for _ in range(20):
+        nq, nk = rng.integers(0, 20, 7), rng.integers(0, 30, 11)
+        qo = np.concatenate([[0], np.cumsum(nq)])
+        ko = np.concatenate([[0], np.cumsum(nk)])
+        ratio = rng.random((7, 11))
+        budget = int(rng.integers(0, qo[-1] * ko[-1] + 1))
+        mask, lst, cnt, keys, used = O.route_global(ratio, qo, ko, budget)
+        cost = nq[:, None] * nk[None, :]
+        assert used == int((cost * mask).sum()) <= budget
+        np.testing.assert_array_equal(keys, (nk[None, :] * mask).sum(axis=1))
+        np.testing.assert_array_equal(cnt, mask.sum(axis=1))
+        # no unselected live block would still fit
+        left = budget - used
+        assert not np.any((mask == 0) & (cost > 0) & (cost <= left))
