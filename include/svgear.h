@@ -9,6 +9,7 @@
  *   svgear_permute   stable cluster-contiguous permutation + means (§3.1, §4.1, §4.3)
  *   svgear_probe     query-centroid error probe -> block ratios    (§4.2, Eq. 5)
  *   svgear_route     greedy error-to-cost selection per query cluster (§4.2, §5)
+ *   svgear_route_global  the same greedy selection under one budget per head (§4.1, §4.2)
  *   svgear_attend    exact selected blocks + centroid compensation (§4.1, §4.3)
  *   svgear_unpermute inverse permutation of the output rows        (§3.1)
  *
@@ -159,6 +160,41 @@ svgear_status svgear_probe(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck
 svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int32_t* k_offsets,
                            int32_t budget_keys, uint8_t* sel_mask, int32_t* sel_list,
                            int32_t* sel_count, int32_t* sel_keys, svgear_stream_t s);
+
+/*
+ * Greedy error-to-cost routing under one budget for the whole attention map of
+ * a head (paper §4.1: at most rho * Nq * Nk exact entries in the block mask;
+ * §4.2: blocks with the highest error-to-size ratio first until the budget is
+ * used). Unlike svgear_route, the budget is not split per query cluster.
+ *
+ * Every block (c, c') whose query cluster and key cluster are both non-empty
+ * competes for `budget_entries` exact (query, key) entries and costs
+ * |q_c| * |k_c'| of them. Blocks are ordered by ratio, highest first; equal
+ * ratios by lower c, then lower c'. Walking that order once, a block is
+ * selected when its cost still fits (blocks that do not fit are passed over;
+ * later, cheaper ones may still fit). budget_entries = floor(rho * Nq * Nk) is
+ * computed by the caller.
+ *
+ *   ratio        [H][Cq][Ck] f32 in (>= 0 for non-empty clusters; NaN and
+ *                negative values count as 0; values of empty clusters are ignored).
+ *   q_offsets    [H][Cq+1] int32 in;  k_offsets [H][Ck+1] int32 in.
+ *   sel_mask     [H][Cq][Ck] uint8 out (1 = exact).
+ *   sel_list     [H][Cq][Ck] int32 out: selected key clusters ascending, -1 padded. May be NULL.
+ *   sel_count    [H][Cq] int32 out. May be NULL.
+ *   sel_keys     [H][Cq] int32 out: exact keys of each query cluster. May be NULL.
+ *   used_entries [H] int64 out: exact entries used (<= budget_entries). May be NULL.
+ *   ws           svgear_route_global_workspace(H, Cq, Ck) bytes (sort buffers).
+ *
+ * Returns SVGEAR_ERR_INVALID_ARG for sizes outside 1..1024, a negative budget
+ * or a NULL required pointer, SVGEAR_ERR_WORKSPACE for a missing or short
+ * workspace; nothing is launched then.
+ */
+size_t svgear_route_global_workspace(int H, int Cq, int Ck);
+svgear_status svgear_route_global(int H, int Cq, int Ck, const float* ratio,
+                                  const int32_t* q_offsets, const int32_t* k_offsets,
+                                  int64_t budget_entries, uint8_t* sel_mask, int32_t* sel_list,
+                                  int32_t* sel_count, int32_t* sel_keys, int64_t* used_entries,
+                                  void* ws, size_t ws_bytes, svgear_stream_t s);
 
 /*
  * Compensated block-sparse attention on permuted Q, K, V (paper §4.1 block

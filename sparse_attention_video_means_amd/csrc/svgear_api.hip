@@ -173,6 +173,25 @@ svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int3
   return SVGEAR_OK;
 }
 
+size_t svgear_route_global_workspace(int H, int Cq, int Ck) {
+  if (H < 1 || Cq < 1 || Ck < 1 || Cq > kMaxClusters || Ck > kMaxClusters) return 0;
+  return route_global_ws_bytes(H, Cq, Ck);
+}
+
+svgear_status svgear_route_global(int H, int Cq, int Ck, const float* ratio,
+                                  const int32_t* q_offsets, const int32_t* k_offsets,
+                                  int64_t budget_entries, uint8_t* sel_mask, int32_t* sel_list,
+                                  int32_t* sel_count, int32_t* sel_keys, int64_t* used_entries,
+                                  void* ws, size_t ws_bytes, svgear_stream_t s) {
+  if (H < 1 || Cq < 1 || Ck < 1 || Cq > kMaxClusters || Ck > kMaxClusters ||
+      budget_entries < 0 || !ratio || !q_offsets || !k_offsets || !sel_mask)
+    return SVGEAR_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < route_global_ws_bytes(H, Cq, Ck)) return SVGEAR_ERR_WORKSPACE;
+  SVG_TRY(launch_route_global(H, Cq, Ck, ratio, q_offsets, k_offsets, budget_entries, sel_mask,
+                              sel_list, sel_count, sel_keys, used_entries, ws, as_stream(s)));
+  return SVGEAR_OK;
+}
+
 size_t svgear_attend_workspace(svgear_dtype dt, int H, int Ck, int d) {
   if (H < 1 || Ck < 1 || Ck > kMaxClusters || elem_bytes(dt) == 0 || !dim_ok(d)) return 0;
   return attend_ws_bytes(elem_bytes(dt), H, Ck, d);

@@ -75,6 +75,11 @@ hipError_t launch_probe(int elem_bytes, int H, int Nk, int d, int Cq, int Ck, fl
 hipError_t launch_route(int H, int Cq, int Ck, const float* ratio, const int32_t* koff,
                         int32_t budget, uint8_t* mask, int32_t* list, int32_t* count,
                         int32_t* keys, hipStream_t s);
+size_t route_global_ws_bytes(int H, int Cq, int Ck);
+hipError_t launch_route_global(int H, int Cq, int Ck, const float* ratio, const int32_t* qoff,
+                               const int32_t* koff, int64_t budget, uint8_t* mask,
+                               int32_t* list, int32_t* count, int32_t* keys, int64_t* used,
+                               void* ws, hipStream_t s);
 
 // attend.hip
 hipError_t launch_attend(int elem_bytes, int H, int Nq, int Nk, int d, int Cq, int Ck,

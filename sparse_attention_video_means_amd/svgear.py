@@ -52,6 +52,9 @@ def lib() -> ctypes.CDLL:
             "svgear_probe": (i32, [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
                                    sz, vp]),
             "svgear_route": (i32, [i32, i32, i32, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]),
+            "svgear_route_global_workspace": (sz, [i32, i32, i32]),
+            "svgear_route_global": (i32, [i32, i32, i32, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
+                                          vp, vp, vp, sz, vp]),
             "svgear_attend_workspace": (sz, [i32, i32, i32, i32]),
             "svgear_attend": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp, sz, vp]),
@@ -67,7 +70,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
            "svgear_permute_workspace", "svgear_permute", "svgear_probe_workspace", "svgear_probe",
-           "svgear_route", "svgear_attend_workspace", "svgear_attend", "svgear_unpermute")
+           "svgear_route", "svgear_route_global_workspace", "svgear_route_global",
+           "svgear_attend_workspace", "svgear_attend", "svgear_unpermute")
 
 
 def _check(fn: str, code: int):
@@ -192,6 +196,31 @@ def svgear_route(ratio, k_offsets, budget_keys: int):
     return mask, lst, cnt, keys
 
 
+def svgear_route_global(ratio, q_offsets, k_offsets, budget_entries: int, ws=None):
+    """Greedy selection under one budget of exact entries per head.
+
+    Returns (mask u8 [H,Cq,Ck], list i32 [H,Cq,Ck], count [H,Cq], keys [H,Cq],
+    used i64 [H])."""
+    _need(ratio, "ratio", torch.float32)
+    H, Cq, Ck = ratio.shape
+    _need(q_offsets, "q_offsets", torch.int32, (H, Cq + 1))
+    _need(k_offsets, "k_offsets", torch.int32, (H, Ck + 1))
+    dev = ratio.device
+    mask = torch.empty((H, Cq, Ck), dtype=torch.uint8, device=dev)
+    lst = torch.empty((H, Cq, Ck), dtype=torch.int32, device=dev)
+    cnt = torch.empty((H, Cq), dtype=torch.int32, device=dev)
+    keys = torch.empty((H, Cq), dtype=torch.int32, device=dev)
+    used = torch.empty((H,), dtype=torch.int64, device=dev)
+    L = lib()
+    if ws is None:
+        ws = _ws(L.svgear_route_global_workspace(H, Cq, Ck), dev)
+    _check("svgear_route_global", L.svgear_route_global(
+        H, Cq, Ck, _ptr(ratio), _ptr(q_offsets), _ptr(k_offsets), int(budget_entries),
+        _ptr(mask), _ptr(lst), _ptr(cnt), _ptr(keys), _ptr(used), _ptr(ws), ws.numel(),
+        _stream()))
+    return mask, lst, cnt, keys, used
+
+
 def svgear_attend(qp, kp, vp, q_offsets, k_offsets, k_centroids, v_centroids, sel_mask,
                   scale: float, out=None):
     """Compensated block-sparse attention on permuted tensors; returns O_p."""
@@ -236,6 +265,8 @@ class RoutedAttention:
     Construct for fixed sizes; each call enqueues cluster(Q), cluster(K),
     permute(Q), permute(K, V), probe, route, attend and unpermute on the
     current stream and returns the output tensor (owned by this object).
+    ``routing`` and ``budget`` are as in ``routed_attention``: exact keys per
+    query cluster ("cluster") or exact entries per head ("global").
     With ``stage_events`` the call also records a HIP event pair around each
     stage (``last_stage_ms()`` reads them after a synchronisation).
     """
@@ -244,7 +275,10 @@ class RoutedAttention:
               "unpermute")
 
     def __init__(self, H, N, d, cq, ck, budget, iters, dtype=torch.bfloat16, device="cuda",
-                 nk=None, scale=None):
+                 nk=None, scale=None, routing="cluster"):
+        if routing not in ("cluster", "global"):
+            raise ValueError(f"routing must be 'cluster' or 'global', not {routing!r}")
+        self.routing = routing
         nq, nk = N, (N if nk is None else nk)
         self.H, self.nq, self.nk, self.d, self.cq, self.ck = H, nq, nk, d, cq, ck
         self.budget, self.iters = int(budget), int(iters)
@@ -263,8 +297,10 @@ class RoutedAttention:
         self.sel_mask = e(H, cq, ck, dt=torch.uint8)
         self.sel_list, self.sel_count, self.sel_keys = e(H, cq, ck), e(H, cq), e(H, cq)
         self.op, self.o = e(H, nq, d, dt=dtype), e(H, nq, d, dt=dtype)
+        self.used_entries = e(H, dt=torch.int64)
         L = lib()
-        wsz = max(L.svgear_cluster_workspace(self.dt, H, nq, d, cq),
+        wsz = max(L.svgear_route_global_workspace(H, cq, ck) if routing == "global" else 0,
+                  L.svgear_cluster_workspace(self.dt, H, nq, d, cq),
                   L.svgear_cluster_workspace(self.dt, H, nk, d, ck),
                   L.svgear_permute_workspace(self.dt, H, nq, d, cq),
                   L.svgear_permute_workspace(self.dt, H, nk, d, ck),
@@ -306,10 +342,16 @@ class RoutedAttention:
                                               _ptr(self.kp), _ptr(self.k_bar), _ptr(self.k_off),
                                               _ptr(self.ratio), _ptr(self.log_norm), ws, wn, s))
         mark(9); mark(10)
-        _check("svgear_route", L.svgear_route(H, cq, ck, _ptr(self.ratio), _ptr(self.k_off),
-                                              self.budget, _ptr(self.sel_mask),
-                                              _ptr(self.sel_list), _ptr(self.sel_count),
-                                              _ptr(self.sel_keys), s))
+        if self.routing == "cluster":
+            _check("svgear_route", L.svgear_route(H, cq, ck, _ptr(self.ratio), _ptr(self.k_off),
+                                                  self.budget, _ptr(self.sel_mask),
+                                                  _ptr(self.sel_list), _ptr(self.sel_count),
+                                                  _ptr(self.sel_keys), s))
+        else:
+            _check("svgear_route_global", L.svgear_route_global(
+                H, cq, ck, _ptr(self.ratio), _ptr(self.q_off), _ptr(self.k_off), self.budget,
+                _ptr(self.sel_mask), _ptr(self.sel_list), _ptr(self.sel_count),
+                _ptr(self.sel_keys), _ptr(self.used_entries), ws, wn, s))
         mark(11); mark(12)
         _check("svgear_attend", L.svgear_attend(dt, H, nq, nk, d, cq, ck, self.scale,
                                                 _ptr(self.qp), _ptr(self.kp), _ptr(self.vp),
@@ -335,13 +377,18 @@ def budget_keys(rho: float, nk: int) -> int:
 
 
 def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q, init_k,
-                     scale: float | None = None, labels_q=None, labels_k=None):
+                     scale: float | None = None, labels_q=None, labels_k=None,
+                     routing: str = "cluster"):
     """The whole path: cluster -> permute -> probe -> route -> attend -> unpermute.
 
     ``init_q``/``init_k`` ([H, C, d] f32) are consumed (updated to the final
     centroids). ``labels_q``/``labels_k`` skip the clustering when given.
-    Returns a dict with every intermediate.
+    ``routing="cluster"`` gives every query cluster ``budget`` exact keys;
+    ``routing="global"`` lets all blocks of a head share ``budget`` exact
+    (query, key) entries. Returns a dict with every intermediate.
     """
+    if routing not in ("cluster", "global"):
+        raise ValueError(f"routing must be 'cluster' or 'global', not {routing!r}")
     d = q.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     res = {}
@@ -352,7 +399,11 @@ def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q,
     perm_q, q_off, (qp,), (q_bar,) = svgear_permute(labels_q, cq, [q])
     perm_k, k_off, (kp, vp), (k_bar, v_bar) = svgear_permute(labels_k, ck, [k, v])
     ratio, log_norm = svgear_probe(q_bar, kp, k_bar, k_off, scale)
-    mask, lst, cnt, keys = svgear_route(ratio, k_off, budget)
+    if routing == "cluster":
+        mask, lst, cnt, keys = svgear_route(ratio, k_off, budget)
+    else:
+        mask, lst, cnt, keys, res["used_entries"] = svgear_route_global(ratio, q_off, k_off,
+                                                                        budget)
     op = svgear_attend(qp, kp, vp, q_off, k_off, k_bar, v_bar, mask, scale)
     o = svgear_unpermute(op, perm_q)
     res.update(labels_q=labels_q, labels_k=labels_k, perm_q=perm_q, perm_k=perm_k, q_off=q_off,

@@ -85,6 +85,17 @@ def test_argument_errors_return_before_any_launch(L):
     # route: negative budget, Ck too large
     assert L.svgear_route(1, 4, 4, fake, fake, -1, fake, null, null, null, null) == 1
     assert L.svgear_route(1, 4, 2000, fake, fake, 5, fake, null, null, null, null) == 1
+    # global route: negative budget, Cq too large, short workspace
+    assert L.svgear_route_global(1, 4, 4, fake, fake, fake, -1, fake, null, null, null, null,
+                                 fake, 1 << 30, null) == 1
+    assert L.svgear_route_global(1, 2000, 4, fake, fake, fake, 5, fake, null, null, null, null,
+                                 fake, 1 << 30, null) == 1
+    assert L.svgear_route_global(1, 4, 4, fake, null, fake, 5, fake, null, null, null, null,
+                                 fake, 1 << 30, null) == 1
+    assert L.svgear_route_global_workspace(2, 100, 500) == 2 * 100 * 500 * 16
+    assert L.svgear_route_global_workspace(2, 100, 1025) == 0
+    assert L.svgear_route_global(1, 4, 4, fake, fake, fake, 5, fake, null, null, null, null,
+                                 fake, 16, null) == 3
     # attend: C > N on the key side
     assert L.svgear_attend(1, 1, 100, 10, 64, 4, 11, 0.1, fake, fake, fake, fake, fake, fake,
                            fake, fake, fake, fake, 1 << 30, null) == 1
