@@ -383,11 +383,12 @@ class RoutedResult(dict):
 
 def routed_attention_head(q, k, v, cq: int, ck: int, budget_keys: int, iters: int,
                           init_q, init_k, scale: float, operand: str = "f64",
-                          labels_q=None, labels_k=None) -> RoutedResult:
+                          labels_q=None, labels_k=None, routing: str = "cluster") -> RoutedResult:
     """cluster -> permute -> probe -> route -> attend -> unpermute for one head.
 
     ``labels_q``/``labels_k`` replace the k-means step when given (parity
-    "given the same cluster assignment").
+    "given the same cluster assignment"). ``routing="global"`` takes
+    ``budget_keys`` as the head's budget of exact entries (``route_global``).
     """
     if labels_q is None:
         labels_q, _, _ = kmeans(q, init_q, iters, operand)
@@ -400,7 +401,10 @@ def routed_attention_head(q, k, v, cq: int, ck: int, budget_keys: int, iters: in
     k_bar = segment_means(kp, k_off)
     v_bar = segment_means(vp, k_off)
     ratio, log_norm = probe(q_bar, kp, k_bar, k_off, scale)
-    mask, lst, cnt, keys = route(ratio, k_off, budget_keys)
+    if routing == "global":
+        mask, lst, cnt, keys, _ = route_global(ratio, q_off, k_off, budget_keys)
+    else:
+        mask, lst, cnt, keys = route(ratio, k_off, budget_keys)
     op = attend(qp, kp, vp, q_off, k_off, k_bar, v_bar, mask, scale)
     o = unpermute(op, perm_q)
     return RoutedResult(labels_q=labels_q, labels_k=labels_k, perm_q=perm_q, perm_k=perm_k,

@@ -116,10 +116,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ ra
 // negatives count as 0) and puts blocks of empty clusters last. A stable LSD
 // radix sort on 8-bit digits, carrying the flat index c * Ck + c', leaves equal
 // ratios in index order, i.e. lower query cluster first, then lower key
-// cluster. Digits that every key shares are skipped. Wavefront 0 then walks
-// the order with the entry budget: whole 64-block windows are taken by prefix
-// sum while they fit; from the first window that overflows on, blocks are
-// taken one at a time in order while they still fit.
+// cluster. Digits that every key shares are skipped. The block then walks
+// the order with the entry budget: whole 1024-block chunks are taken by
+// prefix sum while they fit; from the first chunk that overflows on, blocks
+// are taken one at a time in order while they still fit.
 // route_lists_kernel turns each mask row into the ascending list, the count
 // and the exact keys of the query cluster.
 
@@ -155,9 +155,13 @@ __global__ __launch_bounds__(kGrThreads) void route_global_kernel(
     int32_t* __restrict__ widx) {
   __shared__ int hist_s[4][256];
   __shared__ int base_s[256];
-  __shared__ int wc_s[kGrWaves][256];
+  __shared__ int wc_s[2][kGrWaves][256];  // per-wave digit counts, two tiles in flight
   __shared__ int nq_s[kMaxClusters], nk_s[kMaxClusters];
   __shared__ int scan_s[kGrWaves];
+  __shared__ int64_t tot_s[kGrWaves];
+  __shared__ int64_t cand_cost_s[kGrThreads];
+  __shared__ int cand_idx_s[kGrThreads];
+  __shared__ int64_t used_s;
   const int h = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n = Cq * Ck;
   uint32_t* ka = wkeys + size_t(h) * 2 * n;
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kGrThreads) void route_global_kernel(
   for (int c = tid; c < Ck; c += kGrThreads)
     nk_s[c] = koff[size_t(h) * (Ck + 1) + c + 1] - koff[size_t(h) * (Ck + 1) + c];
   for (int i = tid; i < 4 * 256; i += kGrThreads) (&hist_s[0][0])[i] = 0;
-  for (int i = tid; i < kGrWaves * 256; i += kGrThreads) (&wc_s[0][0])[i] = 0;
+  for (int i = tid; i < 2 * kGrWaves * 256; i += kGrThreads) (&wc_s[0][0][0])[i] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += kGrThreads) {
     const int c = i / Ck, j = i - c * Ck;
@@ -194,11 +198,21 @@ __global__ __launch_bounds__(kGrThreads) void route_global_kernel(
     const int ex = block_exclusive_scan(tid < 256 ? hist_s[p][tid] : 0, scan_s, &tot);
     if (tid < 256) base_s[tid] = ex;
     __syncthreads();
-    for (int t = 0; t < n; t += kGrThreads) {
+    // Tile k (1024 keys) counts into wc_s[k & 1]; the table is cleared while
+    // tile k + 1 counts into the other one, so two barriers per tile suffice.
+    // The next tile's keys are loaded while this one is ranked.
+    uint32_t key_n = (tid < n) ? ks[tid] : 0u;
+    int32_t idx_n = (tid < n) ? is[tid] : 0;
+    for (int t = 0, k = 0; t < n; t += kGrThreads, ++k) {
       const int i = t + tid;
       const bool valid = i < n;
-      const uint32_t key = valid ? ks[i] : 0u;
-      const int32_t idx = valid ? is[i] : 0;
+      const uint32_t key = key_n;
+      const int32_t idx = idx_n;
+      if (i + kGrThreads < n) {
+        key_n = ks[i + kGrThreads];
+        idx_n = is[i + kGrThreads];
+      }
+      int(*wc)[256] = wc_s[k & 1];
       const int dg = (key >> (8 * p)) & 255;
       uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -208,11 +222,11 @@ __global__ __launch_bounds__(kGrThreads) void route_global_kernel(
         peers &= bit ? bal : ~bal;
       }
       const int rank_w = __popcll(peers & below);
-      if (valid && rank_w == 0) wc_s[w][dg] = __popcll(peers);
+      if (valid && rank_w == 0) wc[w][dg] = __popcll(peers);
       __syncthreads();
       if (valid) {
         int off = base_s[dg] + rank_w;
-        for (int v = 0; v < w; ++v) off += wc_s[v][dg];
+        for (int v = 0; v < w; ++v) off += wc[v][dg];
         kd[off] = key;
         id[off] = idx;
       }
@@ -220,53 +234,75 @@ __global__ __launch_bounds__(kGrThreads) void route_global_kernel(
       if (tid < 256) {
         int add = 0;
         for (int v = 0; v < kGrWaves; ++v) {
-          add += wc_s[v][tid];
-          wc_s[v][tid] = 0;
+          add += wc[v][tid];
+          wc[v][tid] = 0;
         }
         base_s[tid] += add;
       }
-      __syncthreads();
     }
+    __syncthreads();
     uint32_t* tk = ks; ks = kd; kd = tk;
     int32_t* ti = is; is = id; id = ti;
   }
 
-  if (w == 0) {
-    int64_t used = 0;
-    bool over = false;
-    for (int t = 0; t < n; t += 64) {
-      const int i = t + lane;
-      const uint32_t key = (i < n) ? ks[i] : kGrDead;
-      const bool live = key != kGrDead;
-      if (__ballot(live) == 0ull) break;  // the blocks of empty clusters sort last
-      const int idx = live ? is[i] : 0;
-      const int c = idx / Ck, j = idx - c * Ck;
-      const int64_t cost = live ? int64_t(nq_s[c]) * nk_s[j] : 0;
-      bool take = false;
-      if (!over) {
-        const int64_t total = shfl64(wave_inclusive_scan64(cost), 63);
-        if (used + total <= budget) {
-          take = live;
-          used += total;
-        } else {
-          over = true;
-        }
+  // Fill, 1024 sorted blocks at a time. Until the first chunk that does not
+  // fit whole, chunks are taken by a block-wide prefix sum of their costs.
+  // From that chunk on, the blocks that could still fit (cost <= the budget
+  // left at the start of the chunk; the budget only shrinks) are compacted in
+  // order into LDS and wavefront 0 walks them one at a time.
+  bool over = false;
+  int64_t used = 0;  // the same in every thread
+  for (int t = 0; t < n; t += kGrThreads) {
+    const int i = t + tid;
+    const uint32_t key = (i < n) ? ks[i] : kGrDead;
+    const bool live = key != kGrDead;
+    if (!__syncthreads_or(live)) break;  // the blocks of empty clusters sort last
+    const int idx = live ? is[i] : 0;
+    const int c = idx / Ck, j = idx - c * Ck;
+    const int64_t cost = live ? int64_t(nq_s[c]) * nk_s[j] : 0;
+    if (!over) {
+      const int64_t incl = wave_inclusive_scan64(cost);
+      if (lane == 63) tot_s[w] = incl;
+      __syncthreads();
+      int64_t total = 0;
+      for (int v = 0; v < kGrWaves; ++v) total += tot_s[v];
+      __syncthreads();
+      if (used + total <= budget) {
+        if (live) mh[idx] = 1;
+        used += total;
+        continue;
       }
-      if (over) {
-        uint64_t pending = __ballot(live);
+      over = true;
+    }
+    const bool cand = live && cost <= budget - used;
+    int ncand;
+    const int pos = block_exclusive_scan(cand ? 1 : 0, scan_s, &ncand);
+    if (cand) {
+      cand_cost_s[pos] = cost;
+      cand_idx_s[pos] = idx;
+    }
+    __syncthreads();
+    if (w == 0) {
+      for (int b = 0; b < ncand; b += 64) {
+        const int q = b + lane;
+        const bool in = q < ncand;
+        const int64_t cq = in ? cand_cost_s[q] : 0;
+        uint64_t pending = __ballot(in);
         while (pending) {
-          const uint64_t fits = __ballot(live && used + cost <= budget) & pending;
+          const uint64_t fits = __ballot(in && used + cq <= budget) & pending;
           if (!fits) break;
           const int f = __ffsll((unsigned long long)fits) - 1;
-          if (lane == f) take = true;
-          used += shfl64(cost, f);
+          if (lane == f) mh[cand_idx_s[q]] = 1;
+          used += shfl64(cq, f);
           pending &= (f == 63) ? 0ull : (~0ull << (f + 1));
         }
       }
-      if (take) mh[idx] = 1;
+      if (lane == 0) used_s = used;
     }
-    if (lane == 0 && used_out) used_out[h] = used;
+    __syncthreads();
+    used = used_s;
   }
+  if (tid == 0 && used_out) used_out[h] = used;
 }
 
 __global__ __launch_bounds__(64) void route_lists_kernel(const uint8_t* __restrict__ mask,
