@@ -35,7 +35,8 @@ import numpy as np
 
 __all__ = [
     "round_operand", "kmeans_assign", "kmeans_update", "kmeans", "permute", "gather",
-    "segment_means", "probe", "route", "route_global", "attend", "unpermute", "dense_attention",
+    "segment_means", "probe", "probe_values", "route", "route_global", "attend", "unpermute",
+    "dense_attention",
     "routed_attention_head", "RoutedResult",
 ]
 
@@ -219,6 +220,51 @@ def probe(q_centroids, kp, k_centroids, k_offsets, scale: float, mode: str = "we
         a, b = int(off[j]), int(off[j + 1])
         if b > a:
             ratio[:, j] = sq[:, a:b].sum(axis=1) / (b - a)
+    log_norm = (m + np.log(z))[:, 0]
+    return ratio, log_norm
+
+
+def probe_values(q_centroids, kp, k_centroids, vp, v_centroids, k_offsets, scale: float):
+    """Value-aware query-centroid error probe (Section 4.2's value-aware estimate).
+
+    The estimate's display did not survive extraction; the text says it brings
+    every v_j and v-bar_j into the error of the compensated output. Reading:
+    the compensation replaces key j's contribution p_cj * v_j to the centroid
+    query's output by p~_cj * v-bar_kappa(j), where p and p~ are the two weights
+    of ``probe`` (exp(s - m)/Z and exp(s~ - m)/Z), and the per-key error is the
+    squared norm of that output gap,
+        eps_cj = || p_cj v_j - p~_cj v-bar_kappa(j) ||^2,
+    aggregated per block as in ``probe``:
+        ratio[c, c'] = (1/|k_c'|) sum_{j in c'} eps_cj.
+    ``probe``'s per-key term (p - p~)^2 is this with every value a unit scalar.
+    ratio = -1 marks an empty key cluster.
+
+    Returns (ratio [Cq, Ck], log_norm [Cq]) as ``probe``.
+    """
+    qc = np.asarray(q_centroids, dtype=np.float64)
+    kp = np.asarray(kp, dtype=np.float64)
+    kc = np.asarray(k_centroids, dtype=np.float64)
+    vp = np.asarray(vp, dtype=np.float64)
+    vc = np.asarray(v_centroids, dtype=np.float64)
+    off = np.asarray(k_offsets)
+    ck = off.shape[0] - 1
+    counts = np.diff(off)
+    kappa = np.repeat(np.arange(ck), counts)
+    vbar = vc[kappa]                                  # [Nk, d]: each key's mean value
+    s = scale * (qc @ kp.T)
+    s_tilde = (scale * (qc @ kc.T))[:, kappa]
+    m = s.max(axis=1, keepdims=True)
+    z = np.exp(s - m).sum(axis=1, keepdims=True)
+    p = np.exp(s - m) / z
+    pt = np.exp(s_tilde - m) / z
+    ratio = np.full((qc.shape[0], ck), -1.0)
+    for c in range(qc.shape[0]):
+        gap = p[c][:, None] * vp - pt[c][:, None] * vbar
+        eps = (gap * gap).sum(axis=1)
+        for j in range(ck):
+            a, b = int(off[j]), int(off[j + 1])
+            if b > a:
+                ratio[c, j] = eps[a:b].sum() / (b - a)
     log_norm = (m + np.log(z))[:, 0]
     return ratio, log_norm
 

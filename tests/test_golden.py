@@ -59,6 +59,16 @@ def test_probe_worked_case():
     assert log_norm[0] == pytest.approx(g["log_norm"], rel=1e-13)
 
 
+def test_probe_values_worked_case():
+    g = load("probe_values_two_keys.txt")
+    keys, values = np.asarray(g["keys"]), np.asarray(g["values"])
+    ratio, log_norm = O.probe_values(np.asarray([g["q_centroid"]]), keys,
+                                     keys.mean(0, keepdims=True), values,
+                                     values.mean(0, keepdims=True), np.asarray([0, 2]), 1.0)
+    assert ratio[0, 0] == pytest.approx(g["ratio"], rel=1e-13)
+    assert log_norm[0] == pytest.approx(g["log_norm"], rel=1e-13)
+
+
 def test_attend_worked_case():
     g = load("attend_density_zero.txt")
     k, v = np.asarray(g["keys"]), np.asarray(g["values"])

@@ -120,6 +120,70 @@ def test_probe_centroid_logit_is_mean_of_block_logits():
             assert np.all(st[:, j] <= s[:, off[j]:off[j + 1]].max(axis=1) + 1e-12)
 
 
+# ---------------------------------------------------------------- value-aware probe
+def _clustered_kv(rng, ck, n_per, d, dv):
+    counts = rng.integers(0, n_per, ck)
+    counts[0] = max(counts[0], 2)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    kp = rng.normal(size=(off[-1], d))
+    vp = rng.normal(size=(off[-1], dv))
+    kc = np.stack([kp[off[j]:off[j + 1]].mean(0) if counts[j] else np.zeros(d)
+                   for j in range(ck)])
+    vc = np.stack([vp[off[j]:off[j + 1]].mean(0) if counts[j] else np.zeros(dv)
+                   for j in range(ck)])
+    return off, kp, kc, vp, vc
+
+
+def test_probe_values_with_values_at_their_means_scales_probe():
+    # v_j = vbar for every key: the gap is (p - p~) vbar, so the value-aware
+    # ratio is ||vbar_c'||^2 times the weight-gap ratio of the same block.
+    rng = np.random.default_rng(70)
+    off, kp, kc, vp, vc = _clustered_kv(rng, 9, 12, 8, 5)
+    kappa = np.repeat(np.arange(9), np.diff(off))
+    qc = rng.normal(size=(4, 8))
+    rv, lv = O.probe_values(qc, kp, kc, vc[kappa], vc, off, 0.7)
+    r, ln = O.probe(qc, kp, kc, off, 0.7)
+    live = np.diff(off) > 0
+    np.testing.assert_allclose(rv[:, live], r[:, live] * (vc[live] ** 2).sum(1)[None, :],
+                               rtol=1e-12, atol=1e-300)
+    assert np.all(rv[:, ~live] == -1)
+    np.testing.assert_allclose(lv, ln, rtol=1e-14)
+
+
+def test_probe_values_identical_keys_leave_the_value_spread():
+    # All keys of a cluster equal: p = p~ = softmax weight of that key, so the
+    # ratio is p^2 times the block's mean squared value deviation.
+    rng = np.random.default_rng(71)
+    ck, d, dv = 6, 5, 3
+    counts = np.array([3, 1, 4, 2, 5, 2])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    kc = rng.normal(size=(ck, d))
+    kp = np.repeat(kc, counts, axis=0)
+    vp = rng.normal(size=(off[-1], dv))
+    vc = np.stack([vp[off[j]:off[j + 1]].mean(0) for j in range(ck)])
+    qc = rng.normal(size=(3, d))
+    rv, _ = O.probe_values(qc, kp, kc, vp, vc, off, 1.3)
+    logits = 1.3 * qc @ kc.T                              # [3, ck], one per cluster
+    lse = logsumexp(logits + np.log(counts)[None, :], axis=1, keepdims=True)
+    pw = np.exp(logits - lse)                             # each key's softmax weight
+    spread = np.array([((vp[off[j]:off[j + 1]] - vc[j]) ** 2).sum(1).mean() for j in range(ck)])
+    np.testing.assert_allclose(rv, pw ** 2 * spread[None, :], rtol=1e-11)
+    assert np.all(rv[:, 1] == 0)  # a one-key cluster is its own mean
+
+
+def test_probe_values_invariant_to_order_inside_clusters():
+    rng = np.random.default_rng(72)
+    off, kp, kc, vp, vc = _clustered_kv(rng, 7, 10, 6, 4)
+    qc = rng.normal(size=(3, 6))
+    perm = np.arange(off[-1])
+    for j in range(7):
+        a, b = off[j], off[j + 1]
+        perm[a:b] = a + rng.permutation(b - a)
+    r1, _ = O.probe_values(qc, kp, kc, vp, vc, off, 0.9)
+    r2, _ = O.probe_values(qc, kp[perm], kc, vp[perm], vc, off, 0.9)
+    np.testing.assert_allclose(r1, r2, rtol=1e-12)
+
+
 # ---------------------------------------------------------------- route
 def test_route_budget_extremes():
     rng = np.random.default_rng(21)
