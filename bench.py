@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--routing", choices=("cluster", "global"), default="cluster",
                     help="exact keys per query cluster (the pages' implementation) or one "
                          "budget of exact entries per head")
+    ap.add_argument("--probe", choices=("weight", "value"), default="weight",
+                    help="block errors from the weight gap or from the value-aware gap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -101,7 +103,7 @@ def budget_for(wl, routing):
     return wl.budget if routing == "cluster" else int(math.floor(wl.rho * wl.n * wl.n))
 
 
-def cpu_baseline(wl, q, k, v, iq, ik, routing):
+def cpu_baseline(wl, q, k, v, iq, ik, routing, probe):
     """The CPU oracle (as written, untuned) on head 0 of the same workload."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -110,7 +112,8 @@ def cpu_baseline(wl, q, k, v, iq, ik, routing):
     f = lambda t: t.float().numpy().astype(np.float64)
     t0 = time.perf_counter()
     O.routed_attention_head(f(q[0]), f(k[0]), f(v[0]), wl.cq, wl.ck, budget_for(wl, routing),
-                            wl.iters, f(iq[0]), f(ik[0]), 1 / math.sqrt(wl.d), routing=routing)
+                            wl.iters, f(iq[0]), f(ik[0]), 1 / math.sqrt(wl.d), routing=routing,
+                            value_aware=probe == "value")
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": dt * 1e3, "unit": "ms/head-layer", "cores": int(threads), "kind": "oracle",
@@ -140,7 +143,7 @@ def main():
     qd, kd, vd, iqd, ikd = (t.to(dev) for t in (q, k, v, iq, ik))
     dtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     ra = svgear.RoutedAttention(wl.heads, wl.n, wl.d, wl.cq, wl.ck, budget_for(wl, args.routing),
-                                wl.iters, dtype, dev, routing=args.routing)
+                                wl.iters, dtype, dev, routing=args.routing, probe=args.probe)
     for _ in range(args.warmup):
         ra(qd, kd, vd, iqd, ikd)
     torch.cuda.synchronize()
@@ -203,7 +206,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on head 0", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, q, k, v, iq, ik, args.routing)
+        cpu = cpu_baseline(wl, q, k, v, iq, ik, args.routing, args.probe)
 
     line = {
         "metric": "routed attn ms/head-layer + executed-block TFLOP/s vs bf16 MFMA peak",
@@ -220,9 +223,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: H={wl.heads} N={wl.n} d={wl.d} {wl.dtype} "
                                f"Cq={wl.cq} Ck={wl.ck} rho={wl.rho} iters={wl.iters}"
-                               + ("" if args.routing == "cluster" else " global routing"),
+                               + ("" if args.routing == "cluster" else " global routing")
+                               + ("" if args.probe == "weight" else " value-aware probe"),
                    "heads": wl.heads, "n": wl.n, "d": wl.d, "cq": wl.cq, "ck": wl.ck,
                    "rho": wl.rho, "iters": wl.iters, "routing": args.routing,
+                   "probe": args.probe,
                    **({"budget_keys": wl.budget} if args.routing == "cluster" else
                       {"budget_entries": budget_for(wl, "global")})},
         "core_ms_per_head_layer": core_ms / wl.heads,
@@ -233,7 +238,8 @@ def main():
         "roofline": {"kernel": "attend_kernel<bf16,128>", "bound": "mfma",
                      "achieved": att_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": att_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic(wl.name) if args.routing == "cluster" else None},
+                     "traffic": measured_traffic(wl.name)
+                     if args.routing == "cluster" and args.probe == "weight" else None},
         "cpu_baseline": cpu,
         **({"dense": extra} if extra else {}),
     }

@@ -8,6 +8,7 @@
  *   svgear_cluster   k-means of each head's Q rows or K rows      (paper §4.1)
  *   svgear_permute   stable cluster-contiguous permutation + means (§3.1, §4.1, §4.3)
  *   svgear_probe     query-centroid error probe -> block ratios    (§4.2, Eq. 5)
+ *   svgear_probe_values  the same probe with the value-aware error   (§4.2, §4.3)
  *   svgear_route     greedy error-to-cost selection per query cluster (§4.2, §5)
  *   svgear_route_global  the same greedy selection under one budget per head (§4.1, §4.2)
  *   svgear_attend    exact selected blocks + centroid compensation (§4.1, §4.3)
@@ -138,6 +139,30 @@ svgear_status svgear_probe(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck
                            const float* q_centroids, const void* Kp, const float* k_centroids,
                            const int32_t* k_offsets, float* ratio, float* log_norm, void* ws,
                            size_t ws_bytes, svgear_stream_t s);
+
+/*
+ * Value-aware query-centroid error probe (paper §4.2's value-aware estimate,
+ * which brings the values of the linear-compensation output of §4.3 into the
+ * error). Its display was lost; the reading implemented: with the two weights
+ * of svgear_probe, p = exp(s - m)/Z (raw key) and p~ = exp(s~ - m)/Z (key
+ * centroid), key j of key cluster c' contributes
+ *     eps_cj = || p_cj v_j - p~_cj vbar_c' ||^2
+ * and ratio[c][c'] = (1/|k_c'|) sum_{j in c'} eps_cj.
+ *
+ * Arguments as svgear_probe, plus
+ *   Vp          [H][Nk][d] dt (permuted values, the keys' order);
+ *   v_centroids [H][Ck][d] f32 (mean value of every key cluster).
+ * The split p^2 ||v_j - vbar||^2 + 2 p (p - p~) (v_j - vbar).vbar + (p - p~)^2 ||vbar||^2
+ * is summed with f32 accumulation from per-key terms computed once per call.
+ * ws: svgear_probe_values_workspace(H, Nk, Cq, Ck) bytes. Errors as svgear_probe.
+ */
+size_t svgear_probe_values_workspace(int H, int Nk, int Cq, int Ck);
+svgear_status svgear_probe_values(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck,
+                                  float scale, const float* q_centroids, const void* Kp,
+                                  const float* k_centroids, const void* Vp,
+                                  const float* v_centroids, const int32_t* k_offsets,
+                                  float* ratio, float* log_norm, void* ws, size_t ws_bytes,
+                                  svgear_stream_t s);
 
 /*
  * Greedy error-to-cost routing per query cluster (paper §4.2 "Error

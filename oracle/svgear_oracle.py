@@ -429,12 +429,14 @@ class RoutedResult(dict):
 
 def routed_attention_head(q, k, v, cq: int, ck: int, budget_keys: int, iters: int,
                           init_q, init_k, scale: float, operand: str = "f64",
-                          labels_q=None, labels_k=None, routing: str = "cluster") -> RoutedResult:
+                          labels_q=None, labels_k=None, routing: str = "cluster",
+                          value_aware: bool = False) -> RoutedResult:
     """cluster -> permute -> probe -> route -> attend -> unpermute for one head.
 
     ``labels_q``/``labels_k`` replace the k-means step when given (parity
     "given the same cluster assignment"). ``routing="global"`` takes
-    ``budget_keys`` as the head's budget of exact entries (``route_global``).
+    ``budget_keys`` as the head's budget of exact entries (``route_global``);
+    ``value_aware=True`` ranks blocks with ``probe_values``.
     """
     if labels_q is None:
         labels_q, _, _ = kmeans(q, init_q, iters, operand)
@@ -446,7 +448,10 @@ def routed_attention_head(q, k, v, cq: int, ck: int, budget_keys: int, iters: in
     q_bar = segment_means(qp, q_off)
     k_bar = segment_means(kp, k_off)
     v_bar = segment_means(vp, k_off)
-    ratio, log_norm = probe(q_bar, kp, k_bar, k_off, scale)
+    if value_aware:
+        ratio, log_norm = probe_values(q_bar, kp, k_bar, vp, v_bar, k_off, scale)
+    else:
+        ratio, log_norm = probe(q_bar, kp, k_bar, k_off, scale)
     if routing == "global":
         mask, lst, cnt, keys, _ = route_global(ratio, q_off, k_off, budget_keys)
     else:

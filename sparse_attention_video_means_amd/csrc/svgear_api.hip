@@ -144,7 +144,30 @@ svgear_status svgear_permute(svgear_dtype dt, int H, int N, int d, int C, const 
 size_t svgear_probe_workspace(int H, int Nk, int Cq, int Ck) {
   if (H < 1 || Nk < 1 || Cq < 1 || Ck < 1 || Ck > Nk || Ck > kMaxClusters || Cq > kMaxClusters)
     return 0;
-  return probe_ws_bytes(H, Nk, Cq, Ck);
+  return probe_ws_bytes(H, Nk, Cq, Ck, false);
+}
+
+size_t svgear_probe_values_workspace(int H, int Nk, int Cq, int Ck) {
+  if (H < 1 || Nk < 1 || Cq < 1 || Ck < 1 || Ck > Nk || Ck > kMaxClusters || Cq > kMaxClusters)
+    return 0;
+  return probe_ws_bytes(H, Nk, Cq, Ck, true);
+}
+
+svgear_status svgear_probe_values(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck,
+                                  float scale, const float* q_centroids, const void* Kp,
+                                  const float* k_centroids, const void* Vp,
+                                  const float* v_centroids, const int32_t* k_offsets,
+                                  float* ratio, float* log_norm, void* ws, size_t ws_bytes,
+                                  svgear_stream_t s) {
+  const svgear_status st = check_shape(dt, H, Nk, d, Ck);
+  if (st != SVGEAR_OK) return st;
+  if (Cq < 1 || Cq > kMaxClusters || !(scale > 0.f) || !q_centroids || !Kp || !k_centroids ||
+      !Vp || !v_centroids || !k_offsets || !ratio)
+    return SVGEAR_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < probe_ws_bytes(H, Nk, Cq, Ck, true)) return SVGEAR_ERR_WORKSPACE;
+  SVG_TRY(launch_probe(elem_bytes(dt), H, Nk, d, Cq, Ck, scale, q_centroids, Kp, k_centroids, Vp,
+                       v_centroids, k_offsets, ws, ratio, log_norm, as_stream(s)));
+  return SVGEAR_OK;
 }
 
 svgear_status svgear_probe(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck, float scale,
@@ -156,9 +179,9 @@ svgear_status svgear_probe(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck
   if (Cq < 1 || Cq > kMaxClusters || !(scale > 0.f) || !q_centroids || !Kp || !k_centroids ||
       !k_offsets || !ratio)
     return SVGEAR_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < probe_ws_bytes(H, Nk, Cq, Ck)) return SVGEAR_ERR_WORKSPACE;
+  if (!ws || ws_bytes < probe_ws_bytes(H, Nk, Cq, Ck, false)) return SVGEAR_ERR_WORKSPACE;
   SVG_TRY(launch_probe(elem_bytes(dt), H, Nk, d, Cq, Ck, scale, q_centroids, Kp, k_centroids,
-                       k_offsets, ws, ratio, log_norm, as_stream(s)));
+                       nullptr, nullptr, k_offsets, ws, ratio, log_norm, as_stream(s)));
   return SVGEAR_OK;
 }
 

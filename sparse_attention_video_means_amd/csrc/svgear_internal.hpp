@@ -66,10 +66,12 @@ hipError_t launch_assign(int elem_bytes, int H, int N, int d, int C, const void*
                          int32_t* hist, hipStream_t s);
 
 // probe.hip
-size_t probe_ws_bytes(int H, int Nk, int Cq, int Ck);
+size_t probe_ws_bytes(int H, int Nk, int Cq, int Ck, bool values);
+// Vp == nullptr: the weight-gap probe; otherwise the value-aware one (vc = vbar).
 hipError_t launch_probe(int elem_bytes, int H, int Nk, int d, int Cq, int Ck, float scale,
-                        const float* qc, const void* Kp, const float* kc, const int32_t* koff,
-                        void* ws, float* ratio, float* log_norm, hipStream_t s);
+                        const float* qc, const void* Kp, const float* kc, const void* Vp,
+                        const float* vc, const int32_t* koff, void* ws, float* ratio,
+                        float* log_norm, hipStream_t s);
 
 // route.hip
 hipError_t launch_route(int H, int Cq, int Ck, const float* ratio, const int32_t* koff,

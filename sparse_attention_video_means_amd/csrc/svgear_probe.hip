@@ -18,6 +18,17 @@
 // accumulated directly (the squared gap is never expanded). A finalize pass
 // rescales the unit triples of each query centroid to the global maximum and
 // forms ratio = E / (Z^2 |k_c'|). No atomics: results are bitwise repeatable.
+//
+// Value-aware variant (§4.2's value-aware estimate; its display was lost, the
+// reading taken is eps = ||p v_j - p~ vbar||^2 with the two weights above). With
+// delta_p = p - p~ it splits as
+//     ||p (v_j - vbar) + delta_p vbar||^2
+//       = p^2 a_j + p delta_p b_j + delta_p^2 w,
+// a_j = ||v_j - vbar||^2, b_j = 2 (v_j - vbar).vbar, w = ||vbar||^2, so that no
+// term is a difference of nearly equal large numbers. value_stats writes
+// (a_j, b_j) per permuted key and w per key cluster; the probe then also
+// streams Ev = sum e (e a_j + dd b_j) (e = exp2(s - m), dd = e - exp2(s~ - m))
+// and the finalize pass forms (Ev + w E) / (Z^2 |k_c'|).
 #include "svgear_common.hpp"
 #include "svgear_internal.hpp"
 
@@ -67,20 +78,74 @@ __device__ __forceinline__ int find_unit_cluster(const int32_t* prefix, int C, i
   return lo;
 }
 
+// (a_j, b_j) = (||v_j - vbar||^2, 2 (v_j - vbar).vbar) for every permuted key j,
+// 16 lanes per key row, 16 rows per block.
 template <typename T, int D>
+__global__ __launch_bounds__(256) void value_stats_kernel(const T* __restrict__ Vp,
+                                                          const float* __restrict__ vc,
+                                                          const int32_t* __restrict__ koff,
+                                                          int Nk, int Ck,
+                                                          float2* __restrict__ stats) {
+  constexpr int EL = D / 16;  // elements per lane
+  const int h = blockIdx.y, tid = threadIdx.x, sub = tid & 15;
+  const int j = blockIdx.x * 16 + (tid >> 4);
+  const bool ok = j < Nk;
+  const int jj = ok ? j : Nk - 1;
+  const int32_t* ko = koff + size_t(h) * (Ck + 1);
+  int lo = 0, hi = Ck;  // the key cluster holding permuted key jj
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ko[mid] <= jj) lo = mid; else hi = mid;
+  }
+  const T* v = Vp + (size_t(h) * Nk + jj) * D + sub * EL;
+  const float* vb = vc + (size_t(h) * Ck + lo) * D + sub * EL;
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) {
+    const float m = vb[e];
+    const float df = to_f32(v[e]) - m;
+    a = fmaf(df, df, a);
+    b = fmaf(df, m, b);
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o, 64);
+    b += __shfl_xor(b, o, 64);
+  }
+  if (ok && sub == 0) stats[size_t(h) * Nk + j] = make_float2(a, 2.f * b);
+}
+
+// w[h][k] = ||vbar_k||^2, one wavefront per key cluster.
+template <int D>
+__global__ __launch_bounds__(256) void vbar_norm_kernel(int Ck, const float* __restrict__ vc,
+                                                        float* __restrict__ w) {
+  const int h = blockIdx.y, k = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (k >= Ck) return;  // whole wavefronts
+  const float* vb = vc + (size_t(h) * Ck + k) * D;
+  float x = 0.f;
+  for (int e = lane; e < D; e += 64) x = fmaf(vb[e], vb[e], x);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  if (lane == 0) w[size_t(h) * Ck + k] = x;
+}
+
+template <typename T, int D, bool VALUE>
 __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc,
                                                     const T* __restrict__ Kp,
                                                     const float* __restrict__ kc,
                                                     const int32_t* __restrict__ koff,
                                                     const int32_t* __restrict__ unit_prefix,
                                                     const float* __restrict__ st2g,
+                                                    const float2* __restrict__ vstat,
                                                     int Nk, int Cq, int Ck, int maxu, float sl2,
                                                     float* __restrict__ rec) {
+  constexpr int RS = VALUE ? 4 : 3;  // floats per unit record
   constexpr int KC = D / 32;
   constexpr int LDR = D + 16 / sizeof(T);
   constexpr int QD = D / 4;  // dims staged per thread (4 threads per key row)
   __shared__ __attribute__((aligned(16))) T ks[64 * LDR];
   __shared__ __attribute__((aligned(16))) T kl[sizeof(T) == 2 ? 64 * LDR : 8];
+  __shared__ __attribute__((aligned(16))) float2 vs[VALUE ? 64 : 2];  // (a_j, b_j) of the tile
 
   const int h = blockIdx.y, grp = blockIdx.z, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
@@ -134,11 +199,13 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
     t.tj = t.j0;
     return t;
   };
-  auto load_raw = [&](const Tile& t, uint4 (&raw)[RAW]) {
+  auto load_raw = [&](const Tile& t, uint4 (&raw)[RAW], float2& vraw) {
     const bool ok = t.tj + srow < t.j1;
     const T* src = Kh + size_t(ok ? t.tj + srow : 0) * D + sq * QD;
 #pragma unroll
     for (int i = 0; i < RAW; ++i) raw[i] = reinterpret_cast<const uint4*>(src)[i];
+    if (VALUE && sq == 0)
+      vraw = ok ? vstat[size_t(h) * Nk + t.tj + srow] : make_float2(0.f, 0.f);
   };
   auto load_kbar = [&](int cc, float (&kb)[QD]) {
     const float* kr = kc + (size_t(h) * Ck + cc) * D + sq * QD;
@@ -152,10 +219,11 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
   if (int(blockIdx.x) >= nunits) return;
   Tile cur = unit_tile(blockIdx.x);
   uint4 raw[RAW];
+  float2 vraw = make_float2(0.f, 0.f);
   float kb[QD], kbn[QD];
-  load_raw(cur, raw);
+  load_raw(cur, raw, vraw);
   load_kbar(cur.cc, kb);
-  float st[2], mp[2], Z[2], E[2], e2[2];
+  float st[2], mp[2], Z[2], E[2], Ev[2], e2[2];
   auto unit_start = [&](int cc) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -163,6 +231,7 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
       mp[cb] = 0.f;  // reference relative to s~: m = s~ + mp, mp >= 0
       Z[cb] = 0.f;
       E[cb] = 0.f;
+      Ev[cb] = 0.f;
       e2[cb] = 1.f;
     }
   };
@@ -188,6 +257,7 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
         *reinterpret_cast<uint4*>(dst + i * E8) = *reinterpret_cast<const uint4*>(out);
         if (kSplit) *reinterpret_cast<uint4*>(dlo + i * E8) = *reinterpret_cast<const uint4*>(rem);
       }
+      if (VALUE && sq == 0) vs[srow] = vraw;
     }
     __syncthreads();
     // the next tile: the rest of this unit, else the first tile of the next
@@ -201,7 +271,7 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
     }
     const bool more = nxt.u < nunits;
     if (more) {
-      load_raw(nxt, raw);
+      load_raw(nxt, raw, vraw);
       if (new_unit) load_kbar(nxt.cc, kbn);
     }
     const int nvalid = min(64, cur.j1 - cur.tj);
@@ -238,8 +308,16 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
           const float al = fast_exp2(mp[cb] - tmax);
           Z[cb] *= al;
           E[cb] *= al * al;
+          if (VALUE) Ev[cb] *= al * al;
           mp[cb] = tmax;
           e2[cb] = fast_exp2(-tmax);
+        }
+        float2 vk[4];
+        if (VALUE) {
+          const float4* vp4 = reinterpret_cast<const float4*>(&vs[kb16 * 16 + g * 4]);
+          const float4 x0 = vp4[0], x1 = vp4[1];
+          vk[0] = make_float2(x0.x, x0.y); vk[1] = make_float2(x0.z, x0.w);
+          vk[2] = make_float2(x1.x, x1.y); vk[3] = make_float2(x1.z, x1.w);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -248,6 +326,7 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
             Z[cb] += e;
             const float dd = e - e2[cb];
             E[cb] = fmaf(dd, dd, E[cb]);
+            if (VALUE) Ev[cb] = fmaf(e, fmaf(dd, vk[i].y, e * vk[i].x), Ev[cb]);
           }
         }
       }
@@ -261,17 +340,20 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
           const float om = __shfl_xor(mp[cb], o, 64);
           const float oZ = __shfl_xor(Z[cb], o, 64);
           const float oE = __shfl_xor(E[cb], o, 64);
+          const float oV = VALUE ? __shfl_xor(Ev[cb], o, 64) : 0.f;
           const float M = fmaxf(mp[cb], om);
           const float a1 = fast_exp2(mp[cb] - M), a2 = fast_exp2(om - M);
           Z[cb] = Z[cb] * a1 + oZ * a2;
           E[cb] = E[cb] * (a1 * a1) + oE * (a2 * a2);
+          if (VALUE) Ev[cb] = Ev[cb] * (a1 * a1) + oV * (a2 * a2);
           mp[cb] = M;
         }
         if (g == 0 && cok[cb]) {
-          float* o = rec + ((size_t(h) * maxu + cur.u) * Cq + cidx[cb]) * 3;
+          float* o = rec + ((size_t(h) * maxu + cur.u) * Cq + cidx[cb]) * RS;
           o[0] = st[cb] + mp[cb];  // absolute base-2 reference of this unit
           o[1] = Z[cb];
           o[2] = E[cb];
+          if (VALUE) o[3] = Ev[cb];
         }
       }
       if (!more) break;
@@ -283,18 +365,21 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
   }
 }
 
+template <bool VALUE>
 __global__ __launch_bounds__(256) void probe_finalize_kernel(int Cq, int Ck, int maxu,
                                                              const int32_t* __restrict__ koff,
                                                              const int32_t* __restrict__ unit_prefix,
                                                              const float* __restrict__ rec,
+                                                             const float* __restrict__ wv,
                                                              float* __restrict__ ratio,
                                                              float* __restrict__ log_norm) {
+  constexpr int RS = VALUE ? 4 : 3;
   __shared__ float red[256];
   const int h = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const int32_t* up = unit_prefix + size_t(h) * (Ck + 1);
   const int32_t* ko = koff + size_t(h) * (Ck + 1);
   const int nu = up[Ck];
-  auto R = [&](int u, int k) { return rec[((size_t(h) * maxu + u) * Cq + c) * 3 + k]; };
+  auto R = [&](int u, int k) { return rec[((size_t(h) * maxu + u) * Cq + c) * RS + k]; };
 
   float mx = -__builtin_inff();
   for (int u = tid; u < nu; u += 256) mx = fmaxf(mx, R(u, 0));
@@ -322,9 +407,10 @@ __global__ __launch_bounds__(256) void probe_finalize_kernel(int Cq, int Ck, int
     float out = (n == 1) ? 0.f : -1.f;
     if (n > 1) {
       float e = 0.f;
+      const float wk = VALUE ? wv[size_t(h) * Ck + k] : 0.f;
       for (int u = up[k]; u < up[k + 1]; ++u) {
         const float a = fast_exp2(R(u, 0) - m);
-        e += R(u, 2) * (a * a);
+        e += (VALUE ? fmaf(R(u, 2), wk, R(u, 3)) : R(u, 2)) * (a * a);
       }
       out = e * inv / float(n);
     }
@@ -333,16 +419,18 @@ __global__ __launch_bounds__(256) void probe_finalize_kernel(int Cq, int Ck, int
   if (tid == 0 && log_norm) log_norm[size_t(h) * Cq + c] = (m + __log2f(Z)) * 0.69314718055994530942f;
 }
 
-size_t probe_ws_bytes(int H, int Nk, int Cq, int Ck) {
+size_t probe_ws_bytes(int H, int Nk, int Cq, int Ck, bool values) {
   return align256(sizeof(int32_t) * size_t(H) * (Ck + 1)) +
          align256(sizeof(float) * size_t(H) * Cq * Ck) +
-         align256(sizeof(float) * 3 * size_t(H) * max_units(Nk, Ck) * Cq);
+         align256(sizeof(float) * (values ? 4 : 3) * size_t(H) * max_units(Nk, Ck) * Cq) +
+         (values ? align256(sizeof(float2) * size_t(H) * Nk) + align256(sizeof(float) * size_t(H) * Ck)
+                 : 0);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool VALUE>
 static hipError_t probe_t(int H, int Nk, int Cq, int Ck, float sl2, const float* qc,
                           const void* Kp, const float* kc, const int32_t* koff, const int32_t* up,
-                          float* st2, float* rec, hipStream_t s) {
+                          float* st2, const float2* vstat, float* rec, hipStream_t s) {
   hipLaunchKernelGGL((centroid_logits_kernel<D>), dim3(ceil_div(Ck, 16), ceil_div(Cq, 16), H),
                      dim3(256), 0, s, Cq, Ck, sl2, qc, kc, st2);
   hipError_t e = hipGetLastError();
@@ -351,34 +439,66 @@ static hipError_t probe_t(int H, int Nk, int Cq, int Ck, float sl2, const float*
   const int groups = ceil_div(Cq, kProbeGroup);
   int per_head = ceil_div(2048, H * groups);
   per_head = per_head < 1 ? 1 : (per_head > maxu ? maxu : per_head);
-  hipLaunchKernelGGL((probe_kernel<T, D>), dim3(per_head, H, groups), dim3(256), 0, s, qc,
-                     static_cast<const T*>(Kp), kc, koff, up, st2, Nk, Cq, Ck, maxu, sl2, rec);
+  hipLaunchKernelGGL((probe_kernel<T, D, VALUE>), dim3(per_head, H, groups), dim3(256), 0, s, qc,
+                     static_cast<const T*>(Kp), kc, koff, up, st2, vstat, Nk, Cq, Ck, maxu, sl2,
+                     rec);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t value_stats_t(int H, int Nk, int Ck, const void* Vp, const float* vc,
+                                const int32_t* koff, float2* stats, float* wv, hipStream_t s) {
+  hipLaunchKernelGGL((value_stats_kernel<T, D>), dim3(ceil_div(Nk, 16), H), dim3(256), 0, s,
+                     static_cast<const T*>(Vp), vc, koff, Nk, Ck, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((vbar_norm_kernel<D>), dim3(ceil_div(Ck, 4), H), dim3(256), 0, s, Ck, vc, wv);
   return hipGetLastError();
 }
 
 hipError_t launch_probe(int elem_bytes, int H, int Nk, int d, int Cq, int Ck, float scale,
-                        const float* qc, const void* Kp, const float* kc, const int32_t* koff,
-                        void* ws, float* ratio, float* log_norm, hipStream_t s) {
+                        const float* qc, const void* Kp, const float* kc, const void* Vp,
+                        const float* vc, const int32_t* koff, void* ws, float* ratio,
+                        float* log_norm, hipStream_t s) {
+  const bool values = Vp != nullptr;
   char* p = static_cast<char*>(ws);
   int32_t* up = reinterpret_cast<int32_t*>(p);
   p += align256(sizeof(int32_t) * size_t(H) * (Ck + 1));
   float* st2 = reinterpret_cast<float*>(p);
   p += align256(sizeof(float) * size_t(H) * Cq * Ck);
   float* rec = reinterpret_cast<float*>(p);
+  p += align256(sizeof(float) * (values ? 4 : 3) * size_t(H) * max_units(Nk, Ck) * Cq);
+  float2* vstat = values ? reinterpret_cast<float2*>(p) : nullptr;
+  if (values) p += align256(sizeof(float2) * size_t(H) * Nk);
+  float* wv = values ? reinterpret_cast<float*>(p) : nullptr;
   hipLaunchKernelGGL(probe_units_kernel, dim3(H), dim3(1024), 0, s, Ck, koff, up);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float sl2 = scale * 1.44269504088896340736f;
-  if (elem_bytes == 2) {
-    e = (d == 128) ? probe_t<__bf16, 128>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, rec, s)
-                   : probe_t<__bf16, 64>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, rec, s);
+  const bool bf = elem_bytes == 2, wide = d == 128;
+  if (values) {
+    e = bf ? (wide ? value_stats_t<__bf16, 128>(H, Nk, Ck, Vp, vc, koff, vstat, wv, s)
+                   : value_stats_t<__bf16, 64>(H, Nk, Ck, Vp, vc, koff, vstat, wv, s))
+           : (wide ? value_stats_t<float, 128>(H, Nk, Ck, Vp, vc, koff, vstat, wv, s)
+                   : value_stats_t<float, 64>(H, Nk, Ck, Vp, vc, koff, vstat, wv, s));
+    if (e != hipSuccess) return e;
+    e = bf ? (wide ? probe_t<__bf16, 128, true>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, vstat, rec, s)
+                   : probe_t<__bf16, 64, true>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, vstat, rec, s))
+           : (wide ? probe_t<float, 128, true>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, vstat, rec, s)
+                   : probe_t<float, 64, true>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, vstat, rec, s));
   } else {
-    e = (d == 128) ? probe_t<float, 128>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, rec, s)
-                   : probe_t<float, 64>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, rec, s);
+    e = bf ? (wide ? probe_t<__bf16, 128, false>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, nullptr, rec, s)
+                   : probe_t<__bf16, 64, false>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, nullptr, rec, s))
+           : (wide ? probe_t<float, 128, false>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, nullptr, rec, s)
+                   : probe_t<float, 64, false>(H, Nk, Cq, Ck, sl2, qc, Kp, kc, koff, up, st2, nullptr, rec, s));
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(probe_finalize_kernel, dim3(Cq, H), dim3(256), 0, s, Cq, Ck,
-                     max_units(Nk, Ck), koff, up, rec, ratio, log_norm);
+  if (values)
+    hipLaunchKernelGGL(probe_finalize_kernel<true>, dim3(Cq, H), dim3(256), 0, s, Cq, Ck,
+                       max_units(Nk, Ck), koff, up, rec, wv, ratio, log_norm);
+  else
+    hipLaunchKernelGGL(probe_finalize_kernel<false>, dim3(Cq, H), dim3(256), 0, s, Cq, Ck,
+                       max_units(Nk, Ck), koff, up, rec, nullptr, ratio, log_norm);
   return hipGetLastError();
 }
 

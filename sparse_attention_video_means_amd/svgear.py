@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
             "svgear_probe_workspace": (sz, [i32, i32, i32, i32]),
             "svgear_probe": (i32, [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
                                    sz, vp]),
+            "svgear_probe_values_workspace": (sz, [i32, i32, i32, i32]),
+            "svgear_probe_values": (i32, [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, sz, vp]),
             "svgear_route": (i32, [i32, i32, i32, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]),
             "svgear_route_global_workspace": (sz, [i32, i32, i32]),
             "svgear_route_global": (i32, [i32, i32, i32, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
@@ -70,6 +73,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
            "svgear_permute_workspace", "svgear_permute", "svgear_probe_workspace", "svgear_probe",
+           "svgear_probe_values_workspace", "svgear_probe_values",
            "svgear_route", "svgear_route_global_workspace", "svgear_route_global",
            "svgear_attend_workspace", "svgear_attend", "svgear_unpermute")
 
@@ -180,6 +184,30 @@ def svgear_probe(q_centroids, kp, k_centroids, k_offsets, scale: float, ws=None)
     return ratio, log_norm
 
 
+def svgear_probe_values(q_centroids, kp, k_centroids, vp, v_centroids, k_offsets, scale: float,
+                        ws=None):
+    """Value-aware block ratios [H, Cq, Ck] and log normalisers [H, Cq]."""
+    _need(kp, "kp")
+    H, Nk, d = kp.shape
+    Cq, Ck = q_centroids.shape[1], k_centroids.shape[1]
+    _need(q_centroids, "q_centroids", torch.float32, (H, Cq, d))
+    _need(k_centroids, "k_centroids", torch.float32, (H, Ck, d))
+    _need(vp, "vp", kp.dtype, (H, Nk, d))
+    _need(v_centroids, "v_centroids", torch.float32, (H, Ck, d))
+    _need(k_offsets, "k_offsets", torch.int32, (H, Ck + 1))
+    ratio = torch.empty((H, Cq, Ck), dtype=torch.float32, device=kp.device)
+    log_norm = torch.empty((H, Cq), dtype=torch.float32, device=kp.device)
+    L = lib()
+    nbytes = L.svgear_probe_values_workspace(H, Nk, Cq, Ck)
+    if ws is None or ws.numel() < nbytes:
+        ws = _ws(nbytes, kp.device)
+    _check("svgear_probe_values", L.svgear_probe_values(
+        _dt(kp), H, Nk, d, Cq, Ck, float(scale), _ptr(q_centroids), _ptr(kp), _ptr(k_centroids),
+        _ptr(vp), _ptr(v_centroids), _ptr(k_offsets), _ptr(ratio), _ptr(log_norm), _ptr(ws),
+        ws.numel(), _stream()))
+    return ratio, log_norm
+
+
 def svgear_route(ratio, k_offsets, budget_keys: int):
     """Greedy selection. Returns (mask u8 [H,Cq,Ck], list i32 [H,Cq,Ck], count [H,Cq], keys [H,Cq])."""
     _need(ratio, "ratio", torch.float32)
@@ -265,8 +293,9 @@ class RoutedAttention:
     Construct for fixed sizes; each call enqueues cluster(Q), cluster(K),
     permute(Q), permute(K, V), probe, route, attend and unpermute on the
     current stream and returns the output tensor (owned by this object).
-    ``routing`` and ``budget`` are as in ``routed_attention``: exact keys per
-    query cluster ("cluster") or exact entries per head ("global").
+    ``routing``, ``budget`` and ``probe`` are as in ``routed_attention``:
+    exact keys per query cluster ("cluster") or exact entries per head
+    ("global"); weight-gap ("weight") or value-aware ("value") block errors.
     With ``stage_events`` the call also records a HIP event pair around each
     stage (``last_stage_ms()`` reads them after a synchronisation).
     """
@@ -275,10 +304,12 @@ class RoutedAttention:
               "unpermute")
 
     def __init__(self, H, N, d, cq, ck, budget, iters, dtype=torch.bfloat16, device="cuda",
-                 nk=None, scale=None, routing="cluster"):
+                 nk=None, scale=None, routing="cluster", probe="weight"):
         if routing not in ("cluster", "global"):
             raise ValueError(f"routing must be 'cluster' or 'global', not {routing!r}")
-        self.routing = routing
+        if probe not in ("weight", "value"):
+            raise ValueError(f"probe must be 'weight' or 'value', not {probe!r}")
+        self.routing, self.probe = routing, probe
         nq, nk = N, (N if nk is None else nk)
         self.H, self.nq, self.nk, self.d, self.cq, self.ck = H, nq, nk, d, cq, ck
         self.budget, self.iters = int(budget), int(iters)
@@ -305,6 +336,7 @@ class RoutedAttention:
                   L.svgear_permute_workspace(self.dt, H, nq, d, cq),
                   L.svgear_permute_workspace(self.dt, H, nk, d, ck),
                   L.svgear_probe_workspace(H, nk, cq, ck),
+                  L.svgear_probe_values_workspace(H, nk, cq, ck) if probe == "value" else 0,
                   L.svgear_attend_workspace(self.dt, H, ck, d))
         self.ws = _ws(wsz, device)
         self._events = None
@@ -338,9 +370,16 @@ class RoutedAttention:
             (vpp * 2)(k.data_ptr(), v.data_ptr()), (vpp * 2)(self.kp.data_ptr(), self.vp.data_ptr()),
             (vpp * 2)(self.k_bar.data_ptr(), self.v_bar.data_ptr()), ws, wn, s))
         mark(7); mark(8)
-        _check("svgear_probe", L.svgear_probe(dt, H, nk, d, cq, ck, self.scale, _ptr(self.q_bar),
-                                              _ptr(self.kp), _ptr(self.k_bar), _ptr(self.k_off),
-                                              _ptr(self.ratio), _ptr(self.log_norm), ws, wn, s))
+        if self.probe == "weight":
+            _check("svgear_probe", L.svgear_probe(
+                dt, H, nk, d, cq, ck, self.scale, _ptr(self.q_bar), _ptr(self.kp),
+                _ptr(self.k_bar), _ptr(self.k_off), _ptr(self.ratio), _ptr(self.log_norm), ws, wn,
+                s))
+        else:
+            _check("svgear_probe_values", L.svgear_probe_values(
+                dt, H, nk, d, cq, ck, self.scale, _ptr(self.q_bar), _ptr(self.kp),
+                _ptr(self.k_bar), _ptr(self.vp), _ptr(self.v_bar), _ptr(self.k_off),
+                _ptr(self.ratio), _ptr(self.log_norm), ws, wn, s))
         mark(9); mark(10)
         if self.routing == "cluster":
             _check("svgear_route", L.svgear_route(H, cq, ck, _ptr(self.ratio), _ptr(self.k_off),
@@ -378,17 +417,20 @@ def budget_keys(rho: float, nk: int) -> int:
 
 def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q, init_k,
                      scale: float | None = None, labels_q=None, labels_k=None,
-                     routing: str = "cluster"):
+                     routing: str = "cluster", probe: str = "weight"):
     """The whole path: cluster -> permute -> probe -> route -> attend -> unpermute.
 
     ``init_q``/``init_k`` ([H, C, d] f32) are consumed (updated to the final
     centroids). ``labels_q``/``labels_k`` skip the clustering when given.
     ``routing="cluster"`` gives every query cluster ``budget`` exact keys;
     ``routing="global"`` lets all blocks of a head share ``budget`` exact
-    (query, key) entries. Returns a dict with every intermediate.
+    (query, key) entries. ``probe="value"`` ranks blocks by the value-aware
+    error instead of the weight gap. Returns a dict with every intermediate.
     """
     if routing not in ("cluster", "global"):
         raise ValueError(f"routing must be 'cluster' or 'global', not {routing!r}")
+    if probe not in ("weight", "value"):
+        raise ValueError(f"probe must be 'weight' or 'value', not {probe!r}")
     d = q.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     res = {}
@@ -398,7 +440,10 @@ def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q,
         labels_k, res["counts_k"] = svgear_cluster(k, init_k, iters)
     perm_q, q_off, (qp,), (q_bar,) = svgear_permute(labels_q, cq, [q])
     perm_k, k_off, (kp, vp), (k_bar, v_bar) = svgear_permute(labels_k, ck, [k, v])
-    ratio, log_norm = svgear_probe(q_bar, kp, k_bar, k_off, scale)
+    if probe == "weight":
+        ratio, log_norm = svgear_probe(q_bar, kp, k_bar, k_off, scale)
+    else:
+        ratio, log_norm = svgear_probe_values(q_bar, kp, k_bar, vp, v_bar, k_off, scale)
     if routing == "cluster":
         mask, lst, cnt, keys = svgear_route(ratio, k_off, budget)
     else:

@@ -85,6 +85,13 @@ def test_argument_errors_return_before_any_launch(L):
     # route: negative budget, Ck too large
     assert L.svgear_route(1, 4, 4, fake, fake, -1, fake, null, null, null, null) == 1
     assert L.svgear_route(1, 4, 2000, fake, fake, 5, fake, null, null, null, null) == 1
+    # value-aware probe: missing values, short workspace
+    assert L.svgear_probe_values(1, 1, 100, 64, 4, 4, 0.1, fake, fake, fake, null, fake, fake,
+                                 fake, null, fake, 1 << 30, null) == 1
+    assert L.svgear_probe_values_workspace(40, 75600, 100, 500) > \
+        L.svgear_probe_workspace(40, 75600, 100, 500)
+    assert L.svgear_probe_values(1, 1, 100, 64, 4, 4, 0.1, fake, fake, fake, fake, fake, fake,
+                                 fake, null, fake, 16, null) == 3
     # global route: negative budget, Cq too large, short workspace
     assert L.svgear_route_global(1, 4, 4, fake, fake, fake, -1, fake, null, null, null, null,
                                  fake, 1 << 30, null) == 1
