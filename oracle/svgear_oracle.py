@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "round_operand", "kmeans_assign", "kmeans_update", "kmeans", "permute", "gather",
     "segment_means", "probe", "probe_values", "route", "route_global", "attend", "unpermute",
-    "dense_attention",
+    "dense_attention", "block_scores", "attention_map_error",
     "routed_attention_head", "RoutedResult",
 ]
 
@@ -416,6 +416,81 @@ def dense_attention(q, k, v, scale: float) -> np.ndarray:
     w = np.exp(s)
     w /= w.sum(axis=1, keepdims=True)
     return w @ v
+
+
+# ----------------------------------------------------------------------------
+# error analysis (Section 5.3, "Strategy of block selection", Fig. 6a)
+# ----------------------------------------------------------------------------
+def block_scores(q_centroids, k_centroids, k_offsets, scale: float):
+    """Score-based block ranking of the top-p baseline (Section 5.3's first two
+    strategies; Sections 1 and 4.2 describe it as selection by approximated
+    attention scores).
+
+    Reading: the score of block (c, c') is its share of the centroid query's
+    attention mass estimated from the centroids,
+        score[c, c'] = |k_c'| exp(scale q-bar_c . k-bar_c') / sum_c'' (same),
+    and the baseline selects blocks in decreasing score. Used as the ``ratio``
+    of ``route`` it fills the same per-query-cluster budget as the error-aware
+    router, which keeps the density of the compared methods equal. Empty key
+    clusters score -1.
+    """
+    qc = np.asarray(q_centroids, dtype=np.float64)
+    kc = np.asarray(k_centroids, dtype=np.float64)
+    n = np.diff(np.asarray(k_offsets)).astype(np.float64)
+    st = scale * (qc @ kc.T)
+    live = n > 0
+    st_live = np.where(live[None, :], st, -np.inf)
+    w = n[None, :] * np.exp(st_live - st_live.max(axis=1, keepdims=True))
+    score = w / w.sum(axis=1, keepdims=True)
+    return np.where(live[None, :], score, -1.0)
+
+
+def attention_map_error(qp, kp, q_offsets, k_offsets, k_centroids, sel_mask, scale: float,
+                        compensate: bool = True):
+    """Distance of a block-sparse attention map from the full one (Section 5.3).
+
+    A_full = softmax(scale Q K^T) row by row. A_sparse keeps the exact weight
+    exp(s_ij) of every key in a selected block of the query's cluster; every
+    key j of a skipped non-empty key cluster c' gets the centroid weight
+    exp(scale q_i . k-bar_c') when ``compensate`` (Section 4.3: the block counts
+    |k_c'| copies of the centroid logit) and 0 when not (top-p without
+    compensation); each sparse row is normalised by its own sum (a row with
+    nothing kept stays 0).
+
+    Returns per query (err [Nq] = sum_j (A_sparse - A_full)_ij^2, z_full [Nq],
+    z_sparse [Nq]), both normalisers taken relative to the row maximum of the
+    exact logits. Section 5.3's mean squared error is err.sum() / (Nq * Nk).
+    """
+    qp = np.asarray(qp, dtype=np.float64)
+    kp = np.asarray(kp, dtype=np.float64)
+    kc = np.asarray(k_centroids, dtype=np.float64)
+    qo, ko = np.asarray(q_offsets), np.asarray(k_offsets)
+    mask = np.asarray(sel_mask)
+    nk = np.diff(ko)
+    kappa = np.repeat(np.arange(nk.size), nk)
+    err = np.zeros(qp.shape[0])
+    zf = np.zeros(qp.shape[0])
+    zs = np.zeros(qp.shape[0])
+    for c in range(qo.size - 1):
+        a, b = int(qo[c]), int(qo[c + 1])
+        if b == a:
+            continue
+        q = qp[a:b]
+        s = scale * (q @ kp.T)                                  # [n, Nk]
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        full = e / e.sum(axis=1, keepdims=True)
+        keep = mask[c][kappa].astype(bool)                      # [Nk]
+        w = np.where(keep[None, :], e, 0.0)
+        if compensate:
+            st = scale * (q @ kc.T)                             # [n, Ck]
+            w = np.where(keep[None, :], w, np.exp(st[:, kappa] - m))
+        z = w.sum(axis=1, keepdims=True)
+        sparse = np.divide(w, z, out=np.zeros_like(w), where=z > 0)
+        err[a:b] = ((sparse - full) ** 2).sum(axis=1)
+        zf[a:b] = e.sum(axis=1)
+        zs[a:b] = z[:, 0]
+    return err, zf, zs
 
 
 # ----------------------------------------------------------------------------

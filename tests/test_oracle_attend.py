@@ -10,6 +10,7 @@ import math
 
 import numpy as np
 import pytest
+from scipy.special import logsumexp
 import torch
 
 from oracle import svgear_oracle as O
@@ -143,3 +144,86 @@ def test_whole_path_routes_to_the_spread_cluster():
     res = O.routed_attention_head(q, k, v, 1, 2, 40, 1, None, None, 0.35, labels_q=lq, labels_k=lk)
     assert list(res.sel_mask[0]) == [0, 1]
     assert res.ratio[0, 1] > 100 * res.ratio[0, 0]
+
+
+# ---------------------------------------------------------------- map error (Section 5.3)
+def _head(rng, n, ck, d, tight=False):
+    counts = rng.multinomial(n, np.ones(ck) / ck)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    kc = rng.normal(size=(ck, d))
+    kp = np.repeat(kc, counts, axis=0)
+    if not tight:
+        kp = kp + 0.5 * rng.normal(size=kp.shape)
+    kbar = np.stack([kp[off[j]:off[j + 1]].mean(0) if counts[j] else kc[j] for j in range(ck)])
+    return off, kp, kbar
+
+
+def test_map_error_full_mask_is_exact():
+    rng = np.random.default_rng(80)
+    off, kp, kbar = _head(rng, 60, 5, 4)
+    qp = rng.normal(size=(20, 4))
+    qo = np.array([0, 8, 20])
+    for comp in (True, False):
+        err, zf, zs = O.attention_map_error(qp, kp, qo, off, kbar, np.ones((2, 5), np.uint8),
+                                            0.8, compensate=comp)
+        assert np.all(err < 1e-30)
+        np.testing.assert_allclose(zs, zf, rtol=1e-14)
+
+
+def test_map_error_identical_keys_compensate_exactly():
+    # keys equal to their centroid: every skipped block's centroid weight is the
+    # exact weight, so the compensated map is the full map at any mask
+    rng = np.random.default_rng(81)
+    off, kp, kbar = _head(rng, 50, 6, 3, tight=True)
+    qp = rng.normal(size=(15, 3))
+    qo = np.array([0, 5, 15])
+    mask = rng.integers(0, 2, (2, 6)).astype(np.uint8)
+    err, zf, zs = O.attention_map_error(qp, kp, qo, off, kbar, mask, 1.1, compensate=True)
+    assert np.all(err < 1e-28)
+    np.testing.assert_allclose(zs, zf, rtol=1e-13)
+
+
+def test_map_error_drop_everything_is_the_squared_map():
+    rng = np.random.default_rng(82)
+    off, kp, kbar = _head(rng, 40, 4, 5)
+    qp = rng.normal(size=(9, 5))
+    qo = np.array([0, 9])
+    err, zf, zs = O.attention_map_error(qp, kp, qo, off, kbar, np.zeros((1, 4), np.uint8), 0.6,
+                                        compensate=False)
+    s = 0.6 * qp @ kp.T
+    a = np.exp(s - logsumexp(s, axis=1, keepdims=True))
+    np.testing.assert_allclose(err, (a ** 2).sum(1), rtol=1e-13)
+    assert np.all(zs == 0)
+    np.testing.assert_allclose(zf, np.exp(logsumexp(s, axis=1) - s.max(1)), rtol=1e-13)
+
+
+def test_map_error_drop_one_block_closed_form():
+    # dropping block B leaves the rest renormalised: with P = mass of B in the
+    # full row, err = sum_{j in B} a_j^2 + (1/(1-P) - 1)^2 sum_{j not in B} a_j^2
+    rng = np.random.default_rng(83)
+    off, kp, kbar = _head(rng, 30, 3, 4)
+    qp = rng.normal(size=(7, 4))
+    mask = np.array([[1, 0, 1]], np.uint8)
+    err, _, _ = O.attention_map_error(qp, kp, np.array([0, 7]), off, kbar, mask, 0.9,
+                                      compensate=False)
+    s = 0.9 * qp @ kp.T
+    a = np.exp(s - logsumexp(s, axis=1, keepdims=True))
+    inb = np.zeros(kp.shape[0], bool)
+    inb[off[1]:off[2]] = True
+    P = a[:, inb].sum(1)
+    want = (a[:, inb] ** 2).sum(1) + (1 / (1 - P) - 1) ** 2 * (a[:, ~inb] ** 2).sum(1)
+    np.testing.assert_allclose(err, want, rtol=1e-11)
+
+
+def test_block_scores_are_centroid_softmax_mass():
+    rng = np.random.default_rng(84)
+    qc, kc = rng.normal(size=(3, 6)), rng.normal(size=(5, 6))
+    off = np.array([0, 4, 4, 9, 10, 16])
+    sc = O.block_scores(qc, kc, off, 0.5)
+    n = np.diff(off)
+    logits = 0.5 * qc @ kc.T
+    live = n > 0
+    want = np.exp(logits[:, live] + np.log(n[live])[None, :]
+                  - logsumexp(logits[:, live] + np.log(n[live])[None, :], axis=1, keepdims=True))
+    np.testing.assert_allclose(sc[:, live], want, rtol=1e-13)
+    assert np.all(sc[:, ~live] == -1)
