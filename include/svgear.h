@@ -11,6 +11,11 @@
  *   svgear_probe_values  the same probe with the value-aware error   (§4.2, §4.3)
  *   svgear_route     greedy error-to-cost selection per query cluster (§4.2, §5)
  *   svgear_route_global  the same greedy selection under one budget per head (§4.1, §4.2)
+ *
+ * and, for the error analysis of block selections (§5.3, Fig. 6a):
+ *
+ *   svgear_block_scores  centroid-estimated attention mass of every block (top-p ranking)
+ *   svgear_map_error     squared distance of a block-sparse attention map from the full one
  *   svgear_attend    exact selected blocks + centroid compensation (§4.1, §4.3)
  *   svgear_unpermute inverse permutation of the output rows        (§3.1)
  *
@@ -253,6 +258,54 @@ svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int C
  */
 svgear_status svgear_unpermute(svgear_dtype dt, int H, int N, int d, const int32_t* perm,
                                const void* Xp, void* X, svgear_stream_t s);
+
+/*
+ * Score-based block ranking of the top-p baseline compared in §5.3 (blocks
+ * selected by approximated attention scores, §1 and §4.2): for every query
+ * centroid c and key cluster c',
+ *     scores[c][c'] = |k_c'| exp(scale qbar_c.kbar_c') / sum over non-empty c''
+ * (the block's share of the centroid query's attention mass estimated from the
+ * centroids), -1 for empty key clusters. Passed to svgear_route as `ratio` it
+ * fills the same budget in decreasing score. f32 throughout.
+ *
+ *   q_centroids [H][Cq][d] f32;  k_centroids [H][Ck][d] f32;  k_offsets [H][Ck+1];
+ *   scores      [H][Cq][Ck] f32 out.
+ * Returns SVGEAR_ERR_INVALID_ARG for sizes outside 1..1024, d not 64 or 128, a
+ * non-positive scale or a NULL pointer.
+ */
+svgear_status svgear_block_scores(int H, int d, int Cq, int Ck, float scale,
+                                  const float* q_centroids, const float* k_centroids,
+                                  const int32_t* k_offsets, float* scores, svgear_stream_t s);
+
+/*
+ * Distance of a block-sparse attention map from the full map (§5.3, "Strategy
+ * of block selection": (1/(Nq Nk)) ||A_sparse - A_full||_F^2, Fig. 6a).
+ *
+ * On permuted queries and keys, A_full is softmax(scale q_i.k_j) over all keys.
+ * A_sparse keeps the exact weight of every key in a block (query cluster of i,
+ * key cluster c') with sel_mask = 1; each key of a skipped non-empty key cluster
+ * gets the centroid weight exp(scale q_i.kbar_c') when `compensate` is non-zero
+ * (§4.3) and 0 otherwise (top-p without compensation); every sparse row is
+ * normalised by its own sum (a row that keeps nothing stays 0).
+ *
+ *   Qp [H][Nq][d], Kp [H][Nk][d] dt;  q_offsets [H][Cq+1], k_offsets [H][Ck+1];
+ *   k_centroids [H][Ck][d] f32;  sel_mask [H][Cq][Ck] uint8;
+ *   err      [H][Nq] f32 out: sum_j (A_sparse - A_full)_ij^2 for each query;
+ *   z_full   [H][Nq] f32 out: sum_j exp(s_ij - max_j s_ij);
+ *   z_sparse [H][Nq] f32 out: the sparse row's normaliser on the same scale.
+ * The caller forms the mean squared error as sum(err) / (Nq Nk) and the
+ * normaliser change as |z_sparse / z_full - 1|. Logits from bf16 (or f32)
+ * matrix cores with f32 accumulation, centroid logits and sums in f32.
+ * ws: svgear_map_error_workspace(H, Nq, Ck) bytes (the centroid logits).
+ * Errors as svgear_attend; SVGEAR_ERR_WORKSPACE for a missing or short workspace.
+ */
+size_t svgear_map_error_workspace(int H, int Nq, int Ck);
+svgear_status svgear_map_error(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
+                               float scale, const void* Qp, const void* Kp,
+                               const int32_t* q_offsets, const int32_t* k_offsets,
+                               const float* k_centroids, const uint8_t* sel_mask, int compensate,
+                               float* err, float* z_full, float* z_sparse, void* ws,
+                               size_t ws_bytes, svgear_stream_t s);
 
 #ifdef __cplusplus
 }

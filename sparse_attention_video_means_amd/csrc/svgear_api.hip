@@ -249,4 +249,40 @@ svgear_status svgear_unpermute(svgear_dtype dt, int H, int N, int d, const int32
   return SVGEAR_OK;
 }
 
+svgear_status svgear_block_scores(int H, int d, int Cq, int Ck, float scale,
+                                  const float* q_centroids, const float* k_centroids,
+                                  const int32_t* k_offsets, float* scores, svgear_stream_t s) {
+  if (H < 1 || Cq < 1 || Ck < 1 || Cq > kMaxClusters || Ck > kMaxClusters || !dim_ok(d) ||
+      !(scale > 0.f) || !q_centroids || !k_centroids || !k_offsets || !scores)
+    return SVGEAR_ERR_INVALID_ARG;
+  SVG_TRY(launch_block_scores(H, d, Cq, Ck, scale, q_centroids, k_centroids, k_offsets, scores,
+                              as_stream(s)));
+  return SVGEAR_OK;
+}
+
+size_t svgear_map_error_workspace(int H, int Nq, int Ck) {
+  if (H < 1 || Nq < 1 || Ck < 1 || Ck > kMaxClusters) return 0;
+  return map_error_ws_bytes(H, Nq, Ck);
+}
+
+svgear_status svgear_map_error(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
+                               float scale, const void* Qp, const void* Kp,
+                               const int32_t* q_offsets, const int32_t* k_offsets,
+                               const float* k_centroids, const uint8_t* sel_mask, int compensate,
+                               float* err, float* z_full, float* z_sparse, void* ws,
+                               size_t ws_bytes, svgear_stream_t s) {
+  svgear_status st = check_shape(dt, H, Nq, d, Cq);
+  if (st != SVGEAR_OK) return st;
+  st = check_shape(dt, H, Nk, d, Ck);
+  if (st != SVGEAR_OK) return st;
+  if (!(scale > 0.f) || !Qp || !Kp || !q_offsets || !k_offsets || !k_centroids || !sel_mask ||
+      !err || !z_full || !z_sparse)
+    return SVGEAR_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < map_error_ws_bytes(H, Nq, Ck)) return SVGEAR_ERR_WORKSPACE;
+  SVG_TRY(launch_map_error(elem_bytes(dt), H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, q_offsets,
+                           k_offsets, k_centroids, sel_mask, compensate ? 1 : 0, err, z_full,
+                           z_sparse, ws, as_stream(s)));
+  return SVGEAR_OK;
+}
+
 }  // extern "C"

@@ -91,4 +91,15 @@ hipError_t launch_attend(int elem_bytes, int H, int Nq, int Nk, int d, int Cq, i
                          hipStream_t s);
 size_t attend_ws_bytes(int elem_bytes, int H, int Ck, int d);
 
+// analysis.hip
+size_t map_error_ws_bytes(int H, int Nq, int Ck);
+hipError_t launch_map_error(int elem_bytes, int H, int Nq, int Nk, int d, int Cq, int Ck,
+                            float scale, const void* Qp, const void* Kp, const int32_t* qoff,
+                            const int32_t* koff, const float* kc, const uint8_t* mask,
+                            int compensate, float* err, float* zfull, float* zsparse, void* ws,
+                            hipStream_t s);
+hipError_t launch_block_scores(int H, int d, int Cq, int Ck, float scale, const float* qc,
+                               const float* kc, const int32_t* koff, float* scores,
+                               hipStream_t s);
+
 }  // namespace svg

@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
             "svgear_attend": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp, sz, vp]),
             "svgear_unpermute": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
+            "svgear_block_scores": (i32, [i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]),
+            "svgear_map_error_workspace": (sz, [i32, i32, i32]),
+            "svgear_map_error": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
+                                       vp, i32, vp, vp, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -75,7 +79,8 @@ EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
            "svgear_permute_workspace", "svgear_permute", "svgear_probe_workspace", "svgear_probe",
            "svgear_probe_values_workspace", "svgear_probe_values",
            "svgear_route", "svgear_route_global_workspace", "svgear_route_global",
-           "svgear_attend_workspace", "svgear_attend", "svgear_unpermute")
+           "svgear_attend_workspace", "svgear_attend", "svgear_unpermute",
+           "svgear_block_scores", "svgear_map_error_workspace", "svgear_map_error")
 
 
 def _check(fn: str, code: int):
@@ -413,6 +418,43 @@ class RoutedAttention:
 def budget_keys(rho: float, nk: int) -> int:
     """floor(rho * N_k), evaluated in double precision on the host."""
     return int(math.floor(float(rho) * nk))
+
+
+def svgear_block_scores(q_centroids, k_centroids, k_offsets, scale: float):
+    """Centroid-estimated attention mass of every block [H, Cq, Ck] (-1: empty)."""
+    _need(q_centroids, "q_centroids", torch.float32)
+    H, Cq, d = q_centroids.shape
+    Ck = k_centroids.shape[1]
+    _need(k_centroids, "k_centroids", torch.float32, (H, Ck, d))
+    _need(k_offsets, "k_offsets", torch.int32, (H, Ck + 1))
+    scores = torch.empty((H, Cq, Ck), dtype=torch.float32, device=q_centroids.device)
+    _check("svgear_block_scores", lib().svgear_block_scores(
+        H, d, Cq, Ck, float(scale), _ptr(q_centroids), _ptr(k_centroids), _ptr(k_offsets),
+        _ptr(scores), _stream()))
+    return scores
+
+
+def svgear_map_error(qp, kp, q_offsets, k_offsets, k_centroids, sel_mask, scale: float,
+                     compensate: bool = True):
+    """Per-query squared map error and both normalisers, each [H, Nq] f32."""
+    _need(qp, "qp")
+    H, Nq, d = qp.shape
+    Nk = kp.shape[1]
+    Cq, Ck = q_offsets.shape[1] - 1, k_offsets.shape[1] - 1
+    _need(kp, "kp", qp.dtype, (H, Nk, d))
+    _need(q_offsets, "q_offsets", torch.int32, (H, Cq + 1))
+    _need(k_offsets, "k_offsets", torch.int32, (H, Ck + 1))
+    _need(k_centroids, "k_centroids", torch.float32, (H, Ck, d))
+    _need(sel_mask, "sel_mask", torch.uint8, (H, Cq, Ck))
+    dev = qp.device
+    err, zf, zs = (torch.empty((H, Nq), dtype=torch.float32, device=dev) for _ in range(3))
+    L = lib()
+    ws = _ws(L.svgear_map_error_workspace(H, Nq, Ck), dev)
+    _check("svgear_map_error", L.svgear_map_error(
+        _dt(qp), H, Nq, Nk, d, Cq, Ck, float(scale), _ptr(qp), _ptr(kp), _ptr(q_offsets),
+        _ptr(k_offsets), _ptr(k_centroids), _ptr(sel_mask), int(bool(compensate)), _ptr(err),
+        _ptr(zf), _ptr(zs), _ptr(ws), ws.numel(), _stream()))
+    return err, zf, zs
 
 
 def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q, init_k,
