@@ -80,3 +80,16 @@ def test_scores_and_map_error(name):
             assert ok.all(), (mname, comp, int((~ok).sum()))
             np.testing.assert_allclose(f64(zf[h]), w_zf, rtol=1e-4)
             np.testing.assert_allclose(f64(zs[h]), w_zs, rtol=1e-4, atol=1e-30)
+
+
+def test_harness_runs_and_matches_its_budget():
+    from sparse_attention_video_means_amd import analysis
+    print("[analysis] harness on the tiny workload", flush=True)
+    lines = analysis.run("tiny", [0.1, 0.5])
+    for line, rho in zip(lines, (0.1, 0.5)):
+        for name in ("topp_drop", "topp_comp", "error_aware_comp", "value_aware_comp"):
+            rec = line[name]
+            assert np.isfinite(rec["mse"]) and rec["mse"] >= 0
+            assert 0 < rec["density"] <= rho + 1e-12
+        # compensating the same blocks never needs more keys than dropping them
+        assert line["topp_comp"]["density"] == line["topp_drop"]["density"]
