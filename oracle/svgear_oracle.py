@@ -36,7 +36,7 @@ import numpy as np
 __all__ = [
     "round_operand", "kmeans_assign", "kmeans_update", "kmeans", "permute", "gather",
     "segment_means", "probe", "probe_values", "route", "route_global", "attend", "unpermute",
-    "dense_attention", "block_scores", "attention_map_error",
+    "dense_attention", "block_scores", "attention_map_error", "row_spread",
     "routed_attention_head", "RoutedResult",
 ]
 
@@ -491,6 +491,23 @@ def attention_map_error(qp, kp, q_offsets, k_offsets, k_centroids, sel_mask, sca
         zf[a:b] = e.sum(axis=1)
         zs[a:b] = z[:, 0]
     return err, zf, zs
+
+
+def row_spread(xp, offsets, means):
+    """Squared distance of every permuted row from its cluster's mean.
+
+    Section 4's bound on the map error carries a residual proportional to the
+    clustering error of the queries, delta_q^2 (Section 5.3, Fig. 6b, plots it
+    against C_q); its definition did not survive extraction. Reading: the
+    per-row spread ||x_i - xbar_c(i)||^2, whose mean over the rows is the
+    k-means objective per row (reported as delta_q^2) and whose maximum is
+    reported beside it.
+    """
+    xp = np.asarray(xp, dtype=np.float64)
+    mu = np.asarray(means, dtype=np.float64)
+    n = np.diff(np.asarray(offsets))
+    kappa = np.repeat(np.arange(n.size), n)
+    return ((xp - mu[kappa]) ** 2).sum(axis=1)
 
 
 # ----------------------------------------------------------------------------

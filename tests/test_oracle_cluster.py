@@ -135,3 +135,18 @@ def test_synth_tiny_shapes_and_init(name):
     # generation is reproducible and per head
     q2, _, _ = synth.make_qkv(wl, heads=[0])
     assert (q2 == q).all()
+
+
+def test_row_spread_decomposes_the_total_sum_of_squares():
+    # with exact cluster means: sum_i ||x_i - xbar||^2 = sum_i ||x_i||^2 - sum_c n_c ||xbar_c||^2
+    rng = np.random.default_rng(90)
+    counts = np.array([4, 1, 0, 7, 3])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    x = rng.normal(size=(off[-1], 6))
+    mu = np.stack([x[off[c]:off[c + 1]].mean(0) if counts[c] else np.zeros(6) for c in range(5)])
+    d2 = O.row_spread(x, off, mu)
+    assert d2.shape == (off[-1],)
+    want = (x ** 2).sum() - (counts[:, None] * mu ** 2).sum()
+    assert d2.sum() == pytest.approx(want, rel=1e-12)
+    assert d2[off[1]] == 0.0  # a one-row cluster is its own mean
+    np.testing.assert_allclose(d2[:4], ((x[:4] - x[:4].mean(0)) ** 2).sum(1), rtol=1e-13)
