@@ -16,6 +16,7 @@
  *
  *   svgear_block_scores  centroid-estimated attention mass of every block (top-p ranking)
  *   svgear_map_error     squared distance of a block-sparse attention map from the full one
+ *   svgear_row_spread    squared distance of every permuted row from its cluster mean
  *   svgear_attend    exact selected blocks + centroid compensation (§4.1, §4.3)
  *   svgear_unpermute inverse permutation of the output rows        (§3.1)
  *
@@ -306,6 +307,22 @@ svgear_status svgear_map_error(svgear_dtype dt, int H, int Nq, int Nk, int d, in
                                const float* k_centroids, const uint8_t* sel_mask, int compensate,
                                float* err, float* z_full, float* z_sparse, void* ws,
                                size_t ws_bytes, svgear_stream_t s);
+
+/*
+ * Clustering spread of permuted rows (§4's bound on the map error carries a
+ * residual proportional to the queries' clustering error delta_q^2, plotted
+ * against C_q in §5.3 Fig. 6b; its formula was lost). For every permuted row p
+ * of cluster c:
+ *     spread[h][p] = || Xp[h][p] - means[h][c] ||^2   (f32)
+ * The mean over rows is the k-means objective per row (delta_q^2 for Q).
+ *
+ *   Xp [H][N][d] dt (cluster-contiguous rows);  means [H][C][d] f32;
+ *   offsets [H][C+1] int32;  spread [H][N] f32 out.
+ * Errors as svgear_permute's shape checks; NULL pointers are SVGEAR_ERR_INVALID_ARG.
+ */
+svgear_status svgear_row_spread(svgear_dtype dt, int H, int N, int d, int C, const void* Xp,
+                                const float* means, const int32_t* offsets, float* spread,
+                                svgear_stream_t s);
 
 #ifdef __cplusplus
 }

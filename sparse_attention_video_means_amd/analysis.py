@@ -18,6 +18,14 @@ in a video model). One JSON line per density:
 
     python -m sparse_attention_video_means_amd.analysis --workload slice \\
         --densities 0.05,0.1,0.2,0.3
+
+With ``--sweep-cq`` the number of query clusters varies instead (§5.3 "Effect
+of clustering", Fig. 6b): for each C_q the line gives the queries' clustering
+error delta_q^2 (mean squared distance of a query from its cluster mean, and
+the maximum) and the map MSE of the method at one density:
+
+    python -m sparse_attention_video_means_amd.analysis --workload slice \\
+        --sweep-cq 25,50,100,200,300 --densities 0.1
 """
 from __future__ import annotations
 
@@ -73,17 +81,60 @@ def run(workload: str, densities, heads: int | None = None, n: int | None = None
     return out
 
 
+def sweep_cq(workload: str, cqs, rho: float, heads: int | None = None, n: int | None = None):
+    base = synth.WORKLOADS[workload]
+    if heads:
+        base = base.with_(heads=heads)
+    if n:
+        base = base.with_(n=n)
+    dev = "cuda"
+    q, k, v = synth.make_qkv(base, threads=16)
+    ik = synth.kmeans_init(k, base.ck, base.seed, 1)
+    scale = 1 / math.sqrt(base.d)
+    total = float(base.heads) * base.n * base.n
+    budget = int(math.floor(rho * base.n))
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = []
+    for cq in cqs:
+        wl = base.with_(cq=cq)
+        iq = synth.kmeans_init(q, cq, wl.seed, 0)
+        res = svgear.routed_attention(qd, kd, vd, cq, wl.ck, budget, wl.iters, iq.to(dev),
+                                      ik.to(dev), scale)
+        spread = svgear.svgear_row_spread(res["qp"], res["q_bar"], res["q_off"]).double()
+        line = {"workload": f"{wl.name}: H={wl.heads} N={wl.n} d={wl.d} {wl.dtype} "
+                            f"Ck={wl.ck} iters={wl.iters}",
+                "cq": cq, "rho": rho, "budget_keys": budget,
+                "delta_q2_mean": float(spread.mean()), "delta_q2_max": float(spread.max())}
+        scores = svgear.svgear_block_scores(res["q_bar"], res["k_bar"], res["k_off"], scale)
+        for name, ratio in (("error_aware_comp", res["ratio"]), ("topp_comp", scores)):
+            mask, _, _, _ = svgear.svgear_route(ratio, res["k_off"], budget)
+            err, zf, zs = svgear.svgear_map_error(res["qp"], res["kp"], res["q_off"], res["k_off"],
+                                                  res["k_bar"], mask, scale, compensate=True)
+            line[name] = {"mse": float(err.double().sum()) / total,
+                          "normaliser_change": float((zs.double() / zf.double() - 1).abs().mean())}
+        out.append(line)
+        print(json.dumps(line), flush=True)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", default="slice", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--densities", default="0.05,0.1,0.2,0.3")
     ap.add_argument("--heads", type=int, default=None, help="use only this many heads")
     ap.add_argument("--n", type=int, default=None, help="override the token count")
+    ap.add_argument("--sweep-cq", default=None,
+                    help="comma-separated query-cluster counts (uses the first density)")
     args = ap.parse_args(argv)
     if not torch.cuda.is_available():
         print("the analysis runs on the GPU kernels; no GPU is visible", file=sys.stderr)
         return 2
-    run(args.workload, [float(x) for x in args.densities.split(",")], args.heads, args.n)
+    densities = [float(x) for x in args.densities.split(",")]
+    if args.sweep_cq:
+        sweep_cq(args.workload, [int(x) for x in args.sweep_cq.split(",")], densities[0],
+                 args.heads, args.n)
+    else:
+        run(args.workload, densities, args.heads, args.n)
     return 0
 
 

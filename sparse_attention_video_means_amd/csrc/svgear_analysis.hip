@@ -16,6 +16,10 @@
 // block_scores_kernel: score[c][c'] = |k_c'| exp(scale qbar_c.kbar_c') / sum,
 // the centroid estimate of the block's attention mass (top-p ranking); -1 for
 // empty key clusters.
+//
+// row_spread_kernel: ||x_p - xbar_c||^2 for every permuted row (the clustering
+// error whose mean is delta_q^2 for the queries, §5.3 Fig. 6b), 16 lanes per
+// row, f32.
 #include "svgear_common.hpp"
 #include "svgear_internal.hpp"
 
@@ -203,6 +207,52 @@ __global__ __launch_bounds__(256) void block_scores_kernel(int Ck, int D, float 
   for (int c2 = tid; c2 < Ck; c2 += 256)
     scores[(size_t(h) * Cq + c) * Ck + c2] =
         (lg[c2] == -__builtin_inff()) ? -1.f : fast_exp2(lg[c2] - m) * inv;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void row_spread_kernel(const T* __restrict__ Xp,
+                                                         const float* __restrict__ mu,
+                                                         const int32_t* __restrict__ off, int N,
+                                                         int C, float* __restrict__ d2) {
+  constexpr int EL = D / 16;
+  const int h = blockIdx.y, tid = threadIdx.x, sub = tid & 15;
+  const int j = blockIdx.x * 16 + (tid >> 4);
+  const bool ok = j < N;
+  const int jj = ok ? j : N - 1;
+  const int32_t* o = off + size_t(h) * (C + 1);
+  int lo = 0, hi = C;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (o[mid] <= jj) lo = mid; else hi = mid;
+  }
+  const T* x = Xp + (size_t(h) * N + jj) * D + sub * EL;
+  const float* m = mu + (size_t(h) * C + lo) * D + sub * EL;
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) {
+    const float df = to_f32(x[e]) - m[e];
+    a = fmaf(df, df, a);
+  }
+#pragma unroll
+  for (int s2 = 8; s2 > 0; s2 >>= 1) a += __shfl_xor(a, s2, 64);
+  if (ok && sub == 0) d2[size_t(h) * N + j] = a;
+}
+
+hipError_t launch_row_spread(int elem_bytes, int H, int N, int d, int C, const void* Xp,
+                             const float* mu, const int32_t* off, float* d2, hipStream_t s) {
+  const dim3 grid(ceil_div(N, 16), H), block(256);
+  if (elem_bytes == 2) {
+    if (d == 128)
+      hipLaunchKernelGGL((row_spread_kernel<__bf16, 128>), grid, block, 0, s, (const __bf16*)Xp, mu, off, N, C, d2);
+    else
+      hipLaunchKernelGGL((row_spread_kernel<__bf16, 64>), grid, block, 0, s, (const __bf16*)Xp, mu, off, N, C, d2);
+  } else {
+    if (d == 128)
+      hipLaunchKernelGGL((row_spread_kernel<float, 128>), grid, block, 0, s, (const float*)Xp, mu, off, N, C, d2);
+    else
+      hipLaunchKernelGGL((row_spread_kernel<float, 64>), grid, block, 0, s, (const float*)Xp, mu, off, N, C, d2);
+  }
+  return hipGetLastError();
 }
 
 size_t map_error_ws_bytes(int H, int Nq, int Ck) { return sizeof(float) * size_t(H) * Nq * Ck; }

@@ -285,4 +285,15 @@ svgear_status svgear_map_error(svgear_dtype dt, int H, int Nq, int Nk, int d, in
   return SVGEAR_OK;
 }
 
+svgear_status svgear_row_spread(svgear_dtype dt, int H, int N, int d, int C, const void* Xp,
+                                const float* means, const int32_t* offsets, float* spread,
+                                svgear_stream_t s) {
+  const svgear_status st = check_shape(dt, H, N, d, C);
+  if (st != SVGEAR_OK) return st;
+  if (!Xp || !means || !offsets || !spread) return SVGEAR_ERR_INVALID_ARG;
+  SVG_TRY(launch_row_spread(elem_bytes(dt), H, N, d, C, Xp, means, offsets, spread,
+                            as_stream(s)));
+  return SVGEAR_OK;
+}
+
 }  // extern "C"

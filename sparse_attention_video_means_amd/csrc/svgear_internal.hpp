@@ -101,5 +101,7 @@ hipError_t launch_map_error(int elem_bytes, int H, int Nq, int Nk, int d, int Cq
 hipError_t launch_block_scores(int H, int d, int Cq, int Ck, float scale, const float* qc,
                                const float* kc, const int32_t* koff, float* scores,
                                hipStream_t s);
+hipError_t launch_row_spread(int elem_bytes, int H, int N, int d, int C, const void* Xp,
+                             const float* mu, const int32_t* off, float* d2, hipStream_t s);
 
 }  // namespace svg

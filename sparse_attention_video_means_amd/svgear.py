@@ -64,6 +64,7 @@ def lib() -> ctypes.CDLL:
             "svgear_unpermute": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "svgear_block_scores": (i32, [i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]),
             "svgear_map_error_workspace": (sz, [i32, i32, i32]),
+            "svgear_row_spread": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
             "svgear_map_error": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
                                        vp, i32, vp, vp, vp, vp, sz, vp]),
         }
@@ -80,7 +81,8 @@ EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
            "svgear_probe_values_workspace", "svgear_probe_values",
            "svgear_route", "svgear_route_global_workspace", "svgear_route_global",
            "svgear_attend_workspace", "svgear_attend", "svgear_unpermute",
-           "svgear_block_scores", "svgear_map_error_workspace", "svgear_map_error")
+           "svgear_block_scores", "svgear_map_error_workspace", "svgear_map_error",
+           "svgear_row_spread")
 
 
 def _check(fn: str, code: int):
@@ -455,6 +457,20 @@ def svgear_map_error(qp, kp, q_offsets, k_offsets, k_centroids, sel_mask, scale:
         _ptr(k_offsets), _ptr(k_centroids), _ptr(sel_mask), int(bool(compensate)), _ptr(err),
         _ptr(zf), _ptr(zs), _ptr(ws), ws.numel(), _stream()))
     return err, zf, zs
+
+
+def svgear_row_spread(xp, means, offsets):
+    """||xp[h, p] - means[h, cluster(p)]||^2 for every permuted row, [H, N] f32."""
+    _need(xp, "xp")
+    H, N, d = xp.shape
+    C = means.shape[1]
+    _need(means, "means", torch.float32, (H, C, d))
+    _need(offsets, "offsets", torch.int32, (H, C + 1))
+    out = torch.empty((H, N), dtype=torch.float32, device=xp.device)
+    _check("svgear_row_spread", lib().svgear_row_spread(_dt(xp), H, N, d, C, _ptr(xp),
+                                                        _ptr(means), _ptr(offsets), _ptr(out),
+                                                        _stream()))
+    return out
 
 
 def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q, init_k,

@@ -92,7 +92,8 @@ def test_argument_errors_return_before_any_launch(L):
         L.svgear_probe_workspace(40, 75600, 100, 500)
     assert L.svgear_probe_values(1, 1, 100, 64, 4, 4, 0.1, fake, fake, fake, fake, fake, fake,
                                  fake, null, fake, 16, null) == 3
-    # analysis: bad head dimension, short workspace
+    # analysis: bad head dimension, short workspace, null output
+    assert L.svgear_row_spread(1, 1, 100, 64, 4, fake, fake, fake, null, null) == 1
     assert L.svgear_block_scores(1, 96, 4, 4, 0.1, fake, fake, fake, fake, null) == 1
     assert L.svgear_map_error_workspace(2, 1000, 50) == 2 * 1000 * 50 * 4
     assert L.svgear_map_error(1, 1, 100, 100, 64, 4, 4, 0.1, fake, fake, fake, fake, fake, fake,

@@ -72,6 +72,10 @@ def test_scores_and_map_error(name):
         # each query's squared full-map norm: the error of keeping nothing, uncompensated
         norm2, _, _ = O.attention_map_error(qp, kp, qo, ko, kb, np.zeros((wl.cq, wl.ck), np.uint8),
                                             scale, compensate=False)
+        for xp_key, mu_key, off_key in (("qp", "q_bar", "q_off"), ("kp", "k_bar", "k_off")):
+            got = f64(S.svgear_row_spread(res[xp_key], res[mu_key], res[off_key])[h])
+            want = O.row_spread(f64(res[xp_key][h]), f64(res[off_key][h]), f64(res[mu_key][h]))
+            np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6 * want.max())
         for (mname, comp), (err, zf, zs) in out.items():
             w_err, w_zf, w_zs = O.attention_map_error(qp, kp, qo, ko, kb, f64(masks[mname][h]),
                                                       scale, compensate=comp)
@@ -93,3 +97,13 @@ def test_harness_runs_and_matches_its_budget():
             assert 0 < rec["density"] <= rho + 1e-12
         # compensating the same blocks never needs more keys than dropping them
         assert line["topp_comp"]["density"] == line["topp_drop"]["density"]
+
+
+def test_cq_sweep_runs():
+    from sparse_attention_video_means_amd import analysis
+    print("[analysis] C_q sweep on a small slice", flush=True)
+    lines = analysis.sweep_cq("slice", [8, 32], 0.2, heads=1, n=2048)
+    assert lines[0]["delta_q2_mean"] > lines[1]["delta_q2_mean"] > 0
+    for line in lines:
+        assert line["delta_q2_max"] >= line["delta_q2_mean"]
+        assert np.isfinite(line["error_aware_comp"]["mse"])
