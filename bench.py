@@ -172,7 +172,9 @@ def main():
     t_att = stages["attend"] * 1e-3
     att_tflops = (exact + comp) / t_att / 1e12
     exec_tflops = exact / t_att / 1e12
-    core_ms = stages["cluster_q"] + stages["cluster_k"] + stages["probe"] + \
+    # clustering and permutation run fused (one call per tensor), so the core
+    # stages include the permutation
+    core_ms = stages["cluster_permute_q"] + stages["cluster_permute_kv"] + stages["probe"] + \
         stages["route"] + stages["attend"]
 
     extra = {}

@@ -7,6 +7,7 @@
  *
  *   svgear_cluster   k-means of each head's Q rows or K rows      (paper §4.1)
  *   svgear_permute   stable cluster-contiguous permutation + means (§3.1, §4.1, §4.3)
+ *   svgear_cluster_permute  both in one call, the last Lloyd pass doing the permutation
  *   svgear_probe     query-centroid error probe -> block ratios    (§4.2, Eq. 5)
  *   svgear_probe_values  the same probe with the value-aware error   (§4.2, §4.3)
  *   svgear_route     greedy error-to-cost selection per query cluster (§4.2, §5)
@@ -124,6 +125,32 @@ svgear_status svgear_permute(svgear_dtype dt, int H, int N, int d, int C, const 
 
 /* Bytes of workspace svgear_probe needs. */
 size_t svgear_probe_workspace(int H, int Nk, int Cq, int Ck);
+
+/*
+ * svgear_cluster followed by svgear_permute on its labels, in one call
+ * (paper §4.1: Q and K are clustered, then each cluster is made contiguous).
+ * The last Lloyd iteration's counting sort is the final permutation, so its
+ * segment-sum pass also writes the permuted copies and the means, and the
+ * separate permutation's extra read of the inputs and its sort are saved.
+ * Every output is bitwise what the two calls produce.
+ *
+ *   src[0] is the clustered tensor X [H][N][d] dt; src[1] (ntensors = 2) follows
+ *   X's labels (V with K). dst[k] [H][N][d] dt receives src[k] in permuted
+ *   order; means[k] [H][C][d] f32 (entries may be NULL) its segment means (0
+ *   for an empty cluster).
+ *   centroids [H][C][d] f32 in: initial table; out: the k-means centroids (an
+ *   empty cluster keeps its centroid, otherwise the mean of X over the final
+ *   labels). labels [H][N], counts [H][C], perm [H][N], offsets [H][C+1] int32
+ *   out, as in svgear_cluster and svgear_permute.
+ *   ws: svgear_cluster_permute_workspace(dt, H, N, d, C) bytes.
+ * Errors as svgear_cluster and svgear_permute.
+ */
+size_t svgear_cluster_permute_workspace(svgear_dtype dt, int H, int N, int d, int C);
+svgear_status svgear_cluster_permute(svgear_dtype dt, int H, int N, int d, int C, int iters,
+                                     int ntensors, const void* const* src, void* const* dst,
+                                     float* const* means, float* centroids, int32_t* labels,
+                                     int32_t* counts, int32_t* perm, int32_t* offsets, void* ws,
+                                     size_t ws_bytes, svgear_stream_t s);
 
 /*
  * Query-centroid error probe (paper §4.2, Eq. 5) and block error-to-size ratio.

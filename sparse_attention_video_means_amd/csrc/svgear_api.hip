@@ -35,16 +35,18 @@ struct ClusterWs {
   float* norms;
 };
 
-size_t cluster_ws_bytes(int eb, int H, int N, int d, int C) {
-  return sort_ws_bytes(H, N, d, C, 1) + align256(sizeof(int32_t) * size_t(H) * N) +
+// nt: tensors whose segment sums the workspace holds (1 for the k-means
+// iterations; 2 when the last iteration also permutes K and V).
+size_t cluster_ws_bytes(int eb, int H, int N, int d, int C, int nt = 1) {
+  return sort_ws_bytes(H, N, d, C, nt) + align256(sizeof(int32_t) * size_t(H) * N) +
          align256(sizeof(int32_t) * size_t(H) * (C + 1)) + align256(size_t(eb) * H * C * d) +
          align256(sizeof(float) * size_t(H) * C);
 }
 
-ClusterWs cluster_ws_carve(void* ws, int eb, int H, int N, int d, int C) {
+ClusterWs cluster_ws_carve(void* ws, int eb, int H, int N, int d, int C, int nt = 1) {
   ClusterWs w;
-  w.sort = sort_ws_carve(ws, H, N, d, C, 1);
-  char* p = static_cast<char*>(ws) + sort_ws_bytes(H, N, d, C, 1);
+  w.sort = sort_ws_carve(ws, H, N, d, C, nt);
+  char* p = static_cast<char*>(ws) + sort_ws_bytes(H, N, d, C, nt);
   w.perm = reinterpret_cast<int32_t*>(p);
   p += align256(sizeof(int32_t) * size_t(H) * N);
   w.offsets = reinterpret_cast<int32_t*>(p);
@@ -104,6 +106,63 @@ svgear_status svgear_cluster(svgear_dtype dt, int H, int N, int d, int C, int it
     const bool last = it + 1 == iters;
     SVG_TRY(launch_combine(eb, H, d, C, 1, w.offsets, w.sort.chunk_prefix, w.sort.partial, N, means,
                            /*mode=*/1, last ? nullptr : w.table, w.norms, hs));
+  }
+  return SVGEAR_OK;
+}
+
+size_t svgear_cluster_permute_workspace(svgear_dtype dt, int H, int N, int d, int C) {
+  if (check_shape(dt, H, N, d, C) != SVGEAR_OK) return 0;
+  return cluster_ws_bytes(elem_bytes(dt), H, N, d, C, 2);
+}
+
+svgear_status svgear_cluster_permute(svgear_dtype dt, int H, int N, int d, int C, int iters,
+                                     int ntensors, const void* const* src, void* const* dst,
+                                     float* const* means, float* centroids, int32_t* labels,
+                                     int32_t* counts, int32_t* perm, int32_t* offsets, void* ws,
+                                     size_t ws_bytes, svgear_stream_t s) {
+  const svgear_status st = check_shape(dt, H, N, d, C);
+  if (st != SVGEAR_OK) return st;
+  if (iters < 1 || ntensors < 1 || ntensors > 2 || !src || !dst || !centroids || !labels ||
+      !counts || !perm || !offsets)
+    return SVGEAR_ERR_INVALID_ARG;
+  for (int k = 0; k < ntensors; ++k)
+    if (!src[k] || !dst[k] || src[k] == dst[k]) return SVGEAR_ERR_INVALID_ARG;
+  const int eb = elem_bytes(dt);
+  if (!ws || ws_bytes < cluster_ws_bytes(eb, H, N, d, C, 2)) return SVGEAR_ERR_WORKSPACE;
+  const hipStream_t hs = as_stream(s);
+  ClusterWs w = cluster_ws_carve(ws, eb, H, N, d, C, 2);
+  const void* X = src[0];
+  SVG_TRY(launch_table(eb, H, d, C, centroids, w.table, w.norms, hs));
+  for (int it = 0; it < iters; ++it) {
+    const bool last = it + 1 == iters;
+    int32_t* off = last ? offsets : w.offsets;
+    int32_t* pm = last ? perm : w.perm;
+    SVG_TRY(launch_assign(eb, H, N, d, C, X, w.table, w.norms, labels, w.sort.rank, w.sort.hist, hs));
+    SVG_TRY(launch_sort_scan(H, N, C, w.sort.hist, w.sort.sizes, off, counts, w.sort.chunk_prefix,
+                             hs));
+    SVG_TRY(launch_scatter(labels, w.sort.rank, w.sort.hist, off, H, N, C, pm, hs));
+    if (!last) {
+      const void* one[1] = {X};
+      SVG_TRY(launch_segsum(eb, H, N, d, C, pm, off, w.sort.chunk_prefix, 1, one, nullptr,
+                            w.sort.partial, hs));
+      float* cm[1] = {centroids};
+      SVG_TRY(launch_combine(eb, H, d, C, 1, off, w.sort.chunk_prefix, w.sort.partial, N, cm,
+                             /*mode=*/1, w.table, w.norms, hs));
+    } else {
+      // the final labels' permutation: one pass writes the permuted copies and
+      // the segment sums of every tensor
+      SVG_TRY(launch_segsum(eb, H, N, d, C, pm, off, w.sort.chunk_prefix, ntensors, src, dst,
+                            w.sort.partial, hs));
+      float* cm[2] = {centroids, nullptr};
+      SVG_TRY(launch_combine(eb, H, d, C, ntensors, off, w.sort.chunk_prefix, w.sort.partial, N,
+                             cm, /*mode=*/1, nullptr, nullptr, hs));
+      bool any = false;
+      if (means)
+        for (int k = 0; k < ntensors; ++k) any = any || means[k];
+      if (any)
+        SVG_TRY(launch_combine(eb, H, d, C, ntensors, off, w.sort.chunk_prefix, w.sort.partial, N,
+                               means, /*mode=*/0, nullptr, nullptr, hs));
+    }
   }
   return SVGEAR_OK;
 }

@@ -46,6 +46,9 @@ def lib() -> ctypes.CDLL:
             "svgear_cluster_workspace": (sz, [i32, i32, i32, i32, i32]),
             "svgear_cluster": (i32, [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "svgear_permute_workspace": (sz, [i32, i32, i32, i32, i32]),
+            "svgear_cluster_permute_workspace": (sz, [i32, i32, i32, i32, i32]),
+            "svgear_cluster_permute": (i32, [i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, sz, vp]),
             "svgear_permute": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz,
                                      vp]),
             "svgear_probe_workspace": (sz, [i32, i32, i32, i32]),
@@ -77,7 +80,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
-           "svgear_permute_workspace", "svgear_permute", "svgear_probe_workspace", "svgear_probe",
+           "svgear_permute_workspace", "svgear_permute", "svgear_cluster_permute_workspace",
+           "svgear_cluster_permute", "svgear_probe_workspace", "svgear_probe",
            "svgear_probe_values_workspace", "svgear_probe_values",
            "svgear_route", "svgear_route_global_workspace", "svgear_route_global",
            "svgear_attend_workspace", "svgear_attend", "svgear_unpermute",
@@ -168,6 +172,39 @@ def svgear_permute(labels: torch.Tensor, C: int, tensors, with_means: bool = Tru
                                               _ptr(offsets), nt, src, dst, mp, _ptr(ws),
                                               ws.numel(), _stream()))
     return perm, offsets, outs, means
+
+
+def svgear_cluster_permute(tensors, centroids: torch.Tensor, iters: int, with_means: bool = True,
+                           ws=None):
+    """k-means of ``tensors[0]`` and the stable permutation of every tensor by
+    the final labels, in one call. ``centroids`` ([H, C, d] f32) is updated in
+    place. Returns (labels, counts, perm, offsets, permuted tensors, means or None),
+    bitwise what svgear_cluster followed by svgear_permute returns."""
+    tensors = list(tensors)
+    x0 = tensors[0]
+    for i, t in enumerate(tensors):
+        _need(t, f"tensors[{i}]", x0.dtype, x0.shape)
+    H, N, d = x0.shape
+    C = centroids.shape[1]
+    _need(centroids, "centroids", torch.float32, (H, C, d))
+    dev = x0.device
+    e = lambda *shape: torch.empty(shape, dtype=torch.int32, device=dev)
+    labels, counts, perm, offsets = e(H, N), e(H, C), e(H, N), e(H, C + 1)
+    outs = [torch.empty_like(t) for t in tensors]
+    means = [torch.empty((H, C, d), dtype=torch.float32, device=dev) for _ in tensors] \
+        if with_means else None
+    nt = len(tensors)
+    src = (ctypes.c_void_p * nt)(*[t.data_ptr() for t in tensors])
+    dst = (ctypes.c_void_p * nt)(*[t.data_ptr() for t in outs])
+    mp = (ctypes.c_void_p * nt)(*[m.data_ptr() for m in means]) if with_means else None
+    L = lib()
+    nbytes = L.svgear_cluster_permute_workspace(_dt(x0), H, N, d, C)
+    if ws is None or ws.numel() < nbytes:
+        ws = _ws(nbytes, dev)
+    _check("svgear_cluster_permute", L.svgear_cluster_permute(
+        _dt(x0), H, N, d, C, int(iters), nt, src, dst, mp, _ptr(centroids), _ptr(labels),
+        _ptr(counts), _ptr(perm), _ptr(offsets), _ptr(ws), ws.numel(), _stream()))
+    return labels, counts, perm, offsets, outs, means
 
 
 def svgear_probe(q_centroids, kp, k_centroids, k_offsets, scale: float, ws=None):
@@ -297,8 +334,8 @@ def svgear_unpermute(xp, perm, out=None):
 class RoutedAttention:
     """The whole path with every buffer allocated once, for repeated calls.
 
-    Construct for fixed sizes; each call enqueues cluster(Q), cluster(K),
-    permute(Q), permute(K, V), probe, route, attend and unpermute on the
+    Construct for fixed sizes; each call enqueues cluster + permute of Q,
+    cluster + permute of K (with V), probe, route, attend and unpermute on the
     current stream and returns the output tensor (owned by this object).
     ``routing``, ``budget`` and ``probe`` are as in ``routed_attention``:
     exact keys per query cluster ("cluster") or exact entries per head
@@ -307,8 +344,7 @@ class RoutedAttention:
     stage (``last_stage_ms()`` reads them after a synchronisation).
     """
 
-    STAGES = ("cluster_q", "cluster_k", "permute_q", "permute_kv", "probe", "route", "attend",
-              "unpermute")
+    STAGES = ("cluster_permute_q", "cluster_permute_kv", "probe", "route", "attend", "unpermute")
 
     def __init__(self, H, N, d, cq, ck, budget, iters, dtype=torch.bfloat16, device="cuda",
                  nk=None, scale=None, routing="cluster", probe="weight"):
@@ -338,10 +374,8 @@ class RoutedAttention:
         self.used_entries = e(H, dt=torch.int64)
         L = lib()
         wsz = max(L.svgear_route_global_workspace(H, cq, ck) if routing == "global" else 0,
-                  L.svgear_cluster_workspace(self.dt, H, nq, d, cq),
-                  L.svgear_cluster_workspace(self.dt, H, nk, d, ck),
-                  L.svgear_permute_workspace(self.dt, H, nq, d, cq),
-                  L.svgear_permute_workspace(self.dt, H, nk, d, ck),
+                  L.svgear_cluster_permute_workspace(self.dt, H, nq, d, cq),
+                  L.svgear_cluster_permute_workspace(self.dt, H, nk, d, ck),
                   L.svgear_probe_workspace(H, nk, cq, ck),
                   L.svgear_probe_values_workspace(H, nk, cq, ck) if probe == "value" else 0,
                   L.svgear_attend_workspace(self.dt, H, ck, d))
@@ -357,26 +391,21 @@ class RoutedAttention:
         mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
         self.cen_q.copy_(init_q)
         self.cen_k.copy_(init_k)
-        mark(0)
-        _check("svgear_cluster", L.svgear_cluster(dt, H, nq, d, cq, self.iters, _ptr(q),
-                                                  _ptr(self.cen_q), _ptr(self.labels_q),
-                                                  _ptr(self.counts_q), ws, wn, s))
-        mark(1); mark(2)
-        _check("svgear_cluster", L.svgear_cluster(dt, H, nk, d, ck, self.iters, _ptr(k),
-                                                  _ptr(self.cen_k), _ptr(self.labels_k),
-                                                  _ptr(self.counts_k), ws, wn, s))
-        mark(3); mark(4)
         vpp = ctypes.c_void_p
-        _check("svgear_permute", L.svgear_permute(
-            dt, H, nq, d, cq, _ptr(self.labels_q), _ptr(self.perm_q), _ptr(self.q_off), 1,
-            (vpp * 1)(q.data_ptr()), (vpp * 1)(self.qp.data_ptr()),
-            (vpp * 1)(self.q_bar.data_ptr()), ws, wn, s))
-        mark(5); mark(6)
-        _check("svgear_permute", L.svgear_permute(
-            dt, H, nk, d, ck, _ptr(self.labels_k), _ptr(self.perm_k), _ptr(self.k_off), 2,
-            (vpp * 2)(k.data_ptr(), v.data_ptr()), (vpp * 2)(self.kp.data_ptr(), self.vp.data_ptr()),
-            (vpp * 2)(self.k_bar.data_ptr(), self.v_bar.data_ptr()), ws, wn, s))
-        mark(7); mark(8)
+        mark(0)
+        _check("svgear_cluster_permute", L.svgear_cluster_permute(
+            dt, H, nq, d, cq, self.iters, 1, (vpp * 1)(q.data_ptr()),
+            (vpp * 1)(self.qp.data_ptr()), (vpp * 1)(self.q_bar.data_ptr()), _ptr(self.cen_q),
+            _ptr(self.labels_q), _ptr(self.counts_q), _ptr(self.perm_q), _ptr(self.q_off), ws, wn,
+            s))
+        mark(1); mark(2)
+        _check("svgear_cluster_permute", L.svgear_cluster_permute(
+            dt, H, nk, d, ck, self.iters, 2, (vpp * 2)(k.data_ptr(), v.data_ptr()),
+            (vpp * 2)(self.kp.data_ptr(), self.vp.data_ptr()),
+            (vpp * 2)(self.k_bar.data_ptr(), self.v_bar.data_ptr()), _ptr(self.cen_k),
+            _ptr(self.labels_k), _ptr(self.counts_k), _ptr(self.perm_k), _ptr(self.k_off), ws, wn,
+            s))
+        mark(3); mark(4)
         if self.probe == "weight":
             _check("svgear_probe", L.svgear_probe(
                 dt, H, nk, d, cq, ck, self.scale, _ptr(self.q_bar), _ptr(self.kp),
@@ -387,7 +416,7 @@ class RoutedAttention:
                 dt, H, nk, d, cq, ck, self.scale, _ptr(self.q_bar), _ptr(self.kp),
                 _ptr(self.k_bar), _ptr(self.vp), _ptr(self.v_bar), _ptr(self.k_off),
                 _ptr(self.ratio), _ptr(self.log_norm), ws, wn, s))
-        mark(9); mark(10)
+        mark(5); mark(6)
         if self.routing == "cluster":
             _check("svgear_route", L.svgear_route(H, cq, ck, _ptr(self.ratio), _ptr(self.k_off),
                                                   self.budget, _ptr(self.sel_mask),
@@ -398,16 +427,16 @@ class RoutedAttention:
                 H, cq, ck, _ptr(self.ratio), _ptr(self.q_off), _ptr(self.k_off), self.budget,
                 _ptr(self.sel_mask), _ptr(self.sel_list), _ptr(self.sel_count),
                 _ptr(self.sel_keys), _ptr(self.used_entries), ws, wn, s))
-        mark(11); mark(12)
+        mark(7); mark(8)
         _check("svgear_attend", L.svgear_attend(dt, H, nq, nk, d, cq, ck, self.scale,
                                                 _ptr(self.qp), _ptr(self.kp), _ptr(self.vp),
                                                 _ptr(self.q_off), _ptr(self.k_off),
                                                 _ptr(self.k_bar), _ptr(self.v_bar),
                                                 _ptr(self.sel_mask), _ptr(self.op), ws, wn, s))
-        mark(13); mark(14)
+        mark(9); mark(10)
         _check("svgear_unpermute", L.svgear_unpermute(dt, H, nq, d, _ptr(self.perm_q),
                                                       _ptr(self.op), _ptr(self.o), s))
-        mark(15)
+        mark(11)
         self._events = ev
         return self.o
 
@@ -479,7 +508,8 @@ def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q,
     """The whole path: cluster -> permute -> probe -> route -> attend -> unpermute.
 
     ``init_q``/``init_k`` ([H, C, d] f32) are consumed (updated to the final
-    centroids). ``labels_q``/``labels_k`` skip the clustering when given.
+    centroids); clustering and permutation run as one call per tensor.
+    ``labels_q``/``labels_k`` skip the clustering when given.
     ``routing="cluster"`` gives every query cluster ``budget`` exact keys;
     ``routing="global"`` lets all blocks of a head share ``budget`` exact
     (query, key) entries. ``probe="value"`` ranks blocks by the value-aware
@@ -493,11 +523,15 @@ def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q,
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     res = {}
     if labels_q is None:
-        labels_q, res["counts_q"] = svgear_cluster(q, init_q, iters)
+        labels_q, res["counts_q"], perm_q, q_off, (qp,), (q_bar,) = \
+            svgear_cluster_permute([q], init_q, iters)
+    else:
+        perm_q, q_off, (qp,), (q_bar,) = svgear_permute(labels_q, cq, [q])
     if labels_k is None:
-        labels_k, res["counts_k"] = svgear_cluster(k, init_k, iters)
-    perm_q, q_off, (qp,), (q_bar,) = svgear_permute(labels_q, cq, [q])
-    perm_k, k_off, (kp, vp), (k_bar, v_bar) = svgear_permute(labels_k, ck, [k, v])
+        labels_k, res["counts_k"], perm_k, k_off, (kp, vp), (k_bar, v_bar) = \
+            svgear_cluster_permute([k, v], init_k, iters)
+    else:
+        perm_k, k_off, (kp, vp), (k_bar, v_bar) = svgear_permute(labels_k, ck, [k, v])
     if probe == "weight":
         ratio, log_norm = svgear_probe(q_bar, kp, k_bar, k_off, scale)
     else:

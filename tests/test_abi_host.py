@@ -85,6 +85,17 @@ def test_argument_errors_return_before_any_launch(L):
     # route: negative budget, Ck too large
     assert L.svgear_route(1, 4, 4, fake, fake, -1, fake, null, null, null, null) == 1
     assert L.svgear_route(1, 4, 2000, fake, fake, 5, fake, null, null, null, null) == 1
+    # fused cluster + permute: three tensors, aliasing, short workspace
+    two = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert L.svgear_cluster_permute(1, 1, 100, 64, 4, 2, 3, two, two, None, fake, fake, fake,
+                                    fake, fake, fake, 1 << 30, null) == 1
+    assert L.svgear_cluster_permute(1, 1, 100, 64, 4, 2, 2, two, two, None, fake, fake, fake,
+                                    fake, fake, fake, 1 << 30, null) == 1
+    out2 = (ctypes.c_void_p * 2)(0x3000, 0x4000)
+    assert L.svgear_cluster_permute(1, 1, 100, 64, 4, 2, 2, two, out2, None, fake, fake, fake,
+                                    fake, fake, fake, 16, null) == 3
+    assert L.svgear_cluster_permute_workspace(1, 40, 75600, 128, 500) > \
+        L.svgear_cluster_workspace(1, 40, 75600, 128, 500)
     # value-aware probe: missing values, short workspace
     assert L.svgear_probe_values(1, 1, 100, 64, 4, 4, 0.1, fake, fake, fake, null, fake, fake,
                                  fake, null, fake, 1 << 30, null) == 1
