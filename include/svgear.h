@@ -270,6 +270,8 @@ svgear_status svgear_route_global(int H, int Cq, int Ck, const float* ratio,
  *   Op [H][Nq][d] dt out (rows in the permuted query order);
  *   ws  workspace of svgear_attend_workspace(...) bytes (it holds the centroid
  *       rows rounded to dt); may be NULL when that size is 0.
+ * One head's K (and V) must span fewer than 2^32 bytes (Nk * d * element
+ * bytes); larger heads return SVGEAR_ERR_INVALID_ARG.
  */
 size_t svgear_attend_workspace(svgear_dtype dt, int H, int Ck, int d);
 

@@ -292,6 +292,8 @@ svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int C
   if (!(scale > 0.f) || !Qp || !Kp || !Vp || !q_offsets || !k_offsets || !k_centroids ||
       !v_centroids || !sel_mask || !Op)
     return SVGEAR_ERR_INVALID_ARG;
+  // the tile copies address one head's K or V with 32-bit byte offsets
+  if (size_t(Nk) * d * elem_bytes(dt) >= (size_t(1) << 32)) return SVGEAR_ERR_INVALID_ARG;
   const size_t need = attend_ws_bytes(elem_bytes(dt), H, Ck, d);
   if (need > 0 && (!ws || ws_bytes < need)) return SVGEAR_ERR_WORKSPACE;
   SVG_TRY(launch_attend(elem_bytes(dt), H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets,

@@ -66,6 +66,21 @@ struct AttCfg<float> {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Raw buffer resource over [p, p + bytes), bytes < 2^32 (the host checks a
+// head's K or V fits): 32-bit data format, no swizzle.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           int(uint32_t(bytes)), 0x00020000);
+}
+
+// 16 bytes at byte offset voff of [base, base + bytes) into LDS at dst (lane l
+// at dst + 16 l). (Kept out of the kernel: with the buffer builtin written
+// inside the kernel template's body the host pass drops the kernel's stub.)
+__device__ __forceinline__ void copy16_lds(const void* base, size_t bytes, uint32_t voff,
+                                           lds_void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(base, bytes), dst, 16, voff, 0, 0, 0);
+}
+
 // Where the 16-byte piece slot j of a K or V tile comes from (key row of the
 // tile and 16-byte piece of that row), and how the matrix operands are read.
 template <typename T, int D>
@@ -320,7 +335,15 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
     const int j = (w * NI + i) * 64 + lane;
     L::k_slot(j, krow[i], kpc[i]);
     L::v_slot(j, vrow[i], vpc[i]);
+    kpc[i] *= 16;  // byte offset of the piece within its row
+    vpc[i] *= 16;
   }
+  // The copies address rows through buffer resources of this head's tensors:
+  // a 32-bit byte offset per lane (row * row bytes + piece) instead of a
+  // 64-bit pointer, and a wave-uniform LDS destination.
+  constexpr int RB = D * int(sizeof(T));
+  const size_t kv_bytes = size_t(Nk) * RB, cen_bytes = size_t(Ck) * RB;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   // sources of this lane's K and V rows of `tile`, its row bias, and the copies
   auto issue = [&](int tile, T* kd, T* vd, float* bd) {
     const bool exact = tile < nt_exact;  // uniform over the block
@@ -344,15 +367,14 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
       bias = (p0 + lane < ncomp) ? cbias_s[p0 + lane] : -__builtin_inff();
     }
     if (w == 0) bd[lane] = bias;
-    const T* kbase = exact ? Kh : KCh;
-    const T* vbase = exact ? Vh : VCh;
+    const T* kb = exact ? Kh : KCh;
+    const T* vb = exact ? Vh : VCh;
+    const size_t nb = exact ? kv_bytes : cen_bytes;
     // all LDS traffic of this call is above: nothing below touches LDS
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kbase + ksrc[i] * D + kpc[i] * EPT),
-                                       (lds_void*)(kd + (w * NI + i) * 64 * EPT), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vbase + vsrc[i] * D + vpc[i] * EPT),
-                                       (lds_void*)(vd + (w * NI + i) * 64 * EPT), 16, 0, 0);
+      copy16_lds(kb, nb, uint32_t(ksrc[i]) * RB + kpc[i], (lds_void*)(kd + (wu * NI + i) * 64 * EPT));
+      copy16_lds(vb, nb, uint32_t(vsrc[i]) * RB + vpc[i], (lds_void*)(vd + (wu * NI + i) * 64 * EPT));
     }
   };
 
