@@ -399,12 +399,21 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   const float inv_sl2 = 1.f / sl2;
   // running maximum (log2 units), its rescale threshold in raw logit units,
   // and the running denominator of every query of this lane
+  // The row sums of the rounded weights: for bf16 one more MFMA per query
+  // block with an all-ones A operand puts query r's sum in every entry of
+  // column r (no vector adds, no final lane reduction); f32 sums per lane.
+  constexpr bool kOnesSum = sizeof(T) == 2;
+  Frag<T> ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones.v[e] = T(1.0f);
+  f32x4 lacc[QB];
   float mrow[QB], thr[QB], lsum[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     mrow[qb] = -__builtin_inff();
     thr[qb] = -__builtin_inff();
     lsum[qb] = 0.f;
+    lacc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // ---- the pieces of one 32-key half kh (keys 32 kh .. 32 kh + 31 of a tile)
@@ -455,7 +464,8 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
       al[qb] = (mn > mrow[qb]) ? fast_exp2(mrow[qb] - mn) : 1.f;
       mrow[qb] = mn;
       thr[qb] = (mn + kRescaleSlack) * inv_sl2;
-      lsum[qb] *= al[qb];
+      if (kOnesSum) lacc[qb] *= al[qb];
+      else lsum[qb] *= al[qb];
     }
     return true;
   };
@@ -474,7 +484,8 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         pb[qb].v[e] = from_f32<T>(fast_exp2(fmaf(sh[e >> 2][qb][e & 3], sl2, nm)));
-      lsum[qb] = frag_sum(pb[qb], lsum[qb]);
+      if (kOnesSum) mma(lacc[qb], ones, pb[qb]);
+      else lsum[qb] = frag_sum(pb[qb], lsum[qb]);
     }
   };
   auto pv = [&](const Frag<T> (&va)[DB], const Frag<T> (&pb)[QB]) {
@@ -529,7 +540,7 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   T* Oh = Op + size_t(h) * Nq * D;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float inv = 1.f / quad_sum(lsum[qb]);
+    const float inv = 1.f / (kOnesSum ? lacc[qb][0] : quad_sum(lsum[qb]));
     const int qi = qw + qb * 16 + r;
     if (qi < q1) {
 #pragma unroll
