@@ -6,7 +6,8 @@ writing the permuted copies and means, so every output must be bitwise what
 the two separate calls give: labels, counts, centroids, permutation, offsets,
 permuted tensors and segment means. Cases: f32 and bf16, d 64 and 128, one
 and two tensors, a ragged tail, one cluster, one Lloyd iteration, and as many
-clusters as the kernels allow (1024).
+clusters as the kernels allow (1024). A second test checks that Lloyd
+iterations chain exactly through the centroids.
 """
 import pytest
 import torch
@@ -52,3 +53,28 @@ def test_fused_equals_separate_calls(name):
     for a, b in [(labels, labels2), (counts, counts2), (c1, c2), (perm, perm2), (off, off2)] + \
             list(zip(outs, outs2)) + list(zip(means, means2)):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["blobs_bf16_two_tensors", "d64_bf16_two_tensors",
+                                  "tiny_f32_one_tensor", "max_clusters"])
+def test_iterations_chain_exactly(name):
+    # Lloyd iteration T of one call equals a fresh one-iteration call started
+    # from the centroids that T - 1 iterations left: the centroids, their
+    # rounded distance table and the assignment carry nothing else between
+    # iterations.
+    wl, _ = CASES[name]
+    S = sv()
+    _, k, _ = synth.make_qkv(wl)
+    x = k.to(DEV)
+    init = synth.kmeans_init(k, wl.ck, wl.seed, 1).to(DEV)
+    iters = max(wl.iters, 3)
+    print(f"[cluster_permute] iteration chain {name}: iters={iters}", flush=True)
+    c_t = init.clone()
+    labels_t, counts_t = S.svgear_cluster(x, c_t, iters)
+    c_prev = init.clone()
+    S.svgear_cluster(x, c_prev, iters - 1)
+    labels_1, counts_1 = S.svgear_cluster(x, c_prev, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(labels_t, labels_1)
+    assert torch.equal(counts_t, counts_1)
+    assert torch.equal(c_t, c_prev)
