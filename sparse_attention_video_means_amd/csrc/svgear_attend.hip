@@ -14,8 +14,8 @@
 //                    the S^T accumulators)
 // so P never leaves registers.
 //
-// LDS layout. Tiles are filled by global_load_lds_dwordx4, which puts lane
-// l's 16-byte piece at (LDS pointer + 16 l) while its global address is free.
+// LDS layout. Tiles are filled by buffer_load_dwordx4 ... lds, which puts
+// lane l's 16-byte piece at (LDS pointer + 16 l) while its source is free.
 // The copy therefore writes every piece where the matrix operands will read
 // it: for bf16, K in MFMA fragment order (one 1 KB fragment per 16 keys x 32
 // dims, lane order) and V in the order of the transposing read
@@ -38,6 +38,12 @@
 // Per tile the two 32-key halves are skewed so that matrix and vector work
 // of different halves sit next to each other:
 //   S0 | S1 + exp(S0) | PV0 + exp(S1) | PV1
+//
+// Pipeline. bf16 tiles cycle through three LDS buffers: while tile t is
+// computed, tile t+1 is in flight, and the copies of tile t+2 are issued at
+// the end of the step. Each step ends with one wait (this wave's copies of
+// tile t+1) and one barrier. f32 tiles are twice as large and use two
+// buffers, one tile ahead.
 #include "svgear_common.hpp"
 #include "svgear_internal.hpp"
 
@@ -65,6 +71,17 @@ struct AttCfg<float> {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier that leaves the caller's own s_waitcnt in charge: unlike
+// __syncthreads it adds no wait for outstanding loads (tile copies still in
+// flight). The caller has waited for its LDS accesses (lgkmcnt 0) and for the
+// copies the other waves will read; the empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Raw buffer resource over [p, p + bytes), bytes < 2^32 (the host checks a
 // head's K or V fits): 32-bit data format, no swizzle.
@@ -220,15 +237,22 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   constexpr int NI = PIECES / (64 * NW);    // copy instructions per wave, tensor and tile
   static_assert(NI * 64 * NW == PIECES, "tile pieces must split evenly over the waves");
   constexpr int TILE = kAttBK * D;          // elements per tile
+  // bf16 tiles are triple-buffered (copies run two tiles ahead); f32 tiles
+  // are twice as large and double-buffered
+  constexpr int kStages = sizeof(T) == 2 ? 3 : 2;
+  constexpr int kAhead = kStages - 1;
   // two buffers per tensor as distinct objects: the compiler can then tell
   // the asynchronous fill of one from the reads of the other and inserts no
   // wait between them
   __shared__ __attribute__((aligned(16))) T ks0[TILE];
   __shared__ __attribute__((aligned(16))) T ks1[TILE];
+  __shared__ __attribute__((aligned(16))) T ks2[kStages > 2 ? TILE : 8];
   __shared__ __attribute__((aligned(16))) T vs0[TILE];
   __shared__ __attribute__((aligned(16))) T vs1[TILE];
+  __shared__ __attribute__((aligned(16))) T vs2[kStages > 2 ? TILE : 8];
   __shared__ __attribute__((aligned(16))) float bias0[kAttBK];
   __shared__ __attribute__((aligned(16))) float bias1[kAttBK];
+  __shared__ __attribute__((aligned(16))) float bias2[kAttBK];
   // per-block lists, sized by Ck at launch (5 * Ck + 1 words):
   extern __shared__ int lists[];
   int* sel_s = lists;                  // selected key cluster ids, ascending
@@ -378,6 +402,16 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
     }
   };
 
+  // s_waitcnt leaving this wave's copies of the newest kAhead - 1 tiles in
+  // flight (2 NI each): vmcnt = that count, expcnt untouched (7), lgkmcnt 0
+  // (gfx9 field layout: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4]
+  // at [15:14])
+  constexpr int kInFlight = (kAhead - 1) * 2 * NI;
+  static_assert(kInFlight < 64, "vmcnt field");
+  auto wait_copies_but_newest = [&]() {
+    __builtin_amdgcn_s_waitcnt((kInFlight & 15) | (7 << 4) | ((kInFlight >> 4) << 14));
+  };
+
   // ---- Q^T fragments
   const T* Qh = Qp + size_t(h) * Nq * D;
   const int qw = q0 + w * 16 * QB;
@@ -495,18 +529,27 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
       for (int qb = 0; qb < QB; ++qb) mma(o[db][qb], va[db], pb[qb]);
   };
 
-  // one tile: start filling the other buffer with tile+1, compute this one
-  auto step = [&](int tile, const T* kb_s, const T* vb_s, const float* bb_s, T* kn_s, T* vn_s,
-                  float* bn_s) {
-    if (tile + 1 < nt_exact && (tile + 1) * kAttBK == rbase + ROWS) {
-      // the next tile starts a new window of source rows (every wave is past
-      // its reads of the current window: the last barrier)
+  // copies of tile+kAhead into the buffer that tile-1 used. Past the last
+  // tile the copies still run (filler rows), so that every step ends with
+  // the same wait: all but this wave's newest copies.
+  auto copy_ahead = [&](int tile, T* kn_s, T* vn_s, float* bn_s) {
+    const int nxt = tile + kAhead;
+    if (nxt < nt_exact && nxt * kAttBK == rbase + ROWS) {
+      // the tile copied next starts a new window of source rows (every wave
+      // is past its reads of the current window: the last barrier)
       rbase += ROWS;
       fill_rows(rbase);
       __syncthreads();
     }
-    if (tile + 1 < nt_all) issue(tile + 1, kn_s, vn_s, bn_s);
-    if (active) {
+    issue(nxt, kn_s, vn_s, bn_s);
+  };
+  // one tile. Two tiles ahead (bf16), the copies are issued after this
+  // tile's matrix work, so that its first LDS reads start the step; one tile
+  // ahead (f32), before it, so that they overlap it.
+  auto step = [&](int tile, const T* kb_s, const T* vb_s, const float* bb_s, T* kn_s, T* vn_s,
+                  float* bn_s) {
+    if (kAhead == 1) copy_ahead(tile, kn_s, vn_s, bn_s);
+    if (active && tile >= 0) {
       Frag<T> ka0[2][KC], ka1[2][KC], va0[DB], va1[DB], pb0[QB], pb1[QB];
       f32x4 s0[2][QB], s1[2][QB];
       kfrags(ka0, kb_s, 0);
@@ -524,17 +567,32 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
       if (up1) scale_o(al1);    // then O follows l to the new maxima
       pv(va1, pb1);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if (kAhead > 1) copy_ahead(tile, kn_s, vn_s, bn_s);
+    wait_copies_but_newest();
+    lds_barrier();
   };
 
-  issue(0, ks0, vs0, bias0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int tile = 0; tile < nt_all; tile += 2) {
-    step(tile, ks0, vs0, bias0, ks1, vs1, bias1);
-    if (tile + 1 < nt_all) step(tile + 1, ks1, vs1, bias1, ks0, vs0, bias0);
+  // The loop starts kAhead tiles early: those steps only issue copies, so
+  // every copy comes from the issue sites inside the loop, whose LDS
+  // destinations the compiler tells apart (it then inserts no wait between
+  // the copies into one buffer and the reads of another). The guards are
+  // nested so that no path reaches a step without the one before it.
+  if constexpr (kStages == 3) {
+    for (int tile = -2; tile < nt_all; tile += 3) {
+      step(tile, ks1, vs1, bias1, ks0, vs0, bias0);
+      if (tile + 1 < nt_all) {
+        step(tile + 1, ks2, vs2, bias2, ks1, vs1, bias1);
+        if (tile + 2 < nt_all) step(tile + 2, ks0, vs0, bias0, ks2, vs2, bias2);
+      }
+    }
+  } else {
+    for (int tile = -1; tile < nt_all; tile += 2) {
+      step(tile, ks1, vs1, bias1, ks0, vs0, bias0);
+      if (tile + 1 < nt_all) step(tile + 1, ks0, vs0, bias0, ks1, vs1, bias1);
+    }
   }
+  // the filler copies of the last steps land before the block's LDS is freed
+  __builtin_amdgcn_s_waitcnt(0);
 
   if (!active) return;
   T* Oh = Op + size_t(h) * Nq * D;
