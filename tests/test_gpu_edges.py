@@ -241,3 +241,28 @@ def test_selection_larger_than_a_source_row_window():
     lkf = rng.integers(0, 9, size=(1, 3000)).astype(np.int32)
     res = check_path(qf, kf, vf, lqf, lkf, 3, 9, budget=2500)
     assert int(res["sel_keys"].max()) > 1024
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_partial_query_blocks(dtype, d):
+    """Query clusters of every size around the kernel's query-block and
+    wavefront boundaries (blocks of 256 queries for bf16 and 64 for f32,
+    wavefronts of 32 and 16): full, half-full and nearly empty last blocks.
+    One key cluster is shorter than half a tile, and in the second run it is
+    the only key cluster, so every exact tile is mostly filler."""
+    rng = np.random.default_rng(23)
+    sizes_q = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 384, 385]
+    lq = np.concatenate([np.full(s, c, np.int32) for c, s in enumerate(sizes_q)])
+    n = lq.size
+    lq = rng.permutation(lq)[None]
+    sizes_k = [20, 300, 77, 1000, 5, 431] + [0] * 2
+    sizes_k[-1] = n - sum(sizes_k)
+    lk = rng.permutation(np.concatenate([np.full(s, c, np.int32)
+                                         for c, s in enumerate(sizes_k)]))[None]
+    q, k, v = data(1, n, d, dtype, 23)
+    check_path(q, k, v, lq, lk, len(sizes_q), len(sizes_k), budget=1400)
+    # a single selected key cluster shorter than a half tile and nothing to
+    # compensate: the second half of the only tile is all filler
+    lk1 = np.zeros((1, n), np.int32)
+    k1, v1 = k[:, :20].contiguous(), v[:, :20].contiguous()
+    check_path(q, k1, v1, lq, lk1[:, :20], len(sizes_q), 1, budget=20)
