@@ -115,12 +115,15 @@ struct TileLayout<__bf16, D> {
     row = (f / KC) * 16 + (l & 15);
     piece = (f % KC) * 4 + (l >> 4);
   }
-  // transposed read (32-key half h, dim block db, upper 16 keys u) occupies
-  // slots 32 i .. 32 i + 31, i = (h DB + db) 2 + u; lane group g of the read
-  // takes keys 32 h + 16 u + 4 g + e (e = 0..3), 16 dims each, as two pieces
+  // transposed read (32-key half h, upper 16 keys u, dim block db) occupies
+  // slots 32 i .. 32 i + 31, i = (2 h + u) DB + db; lane group g of the read
+  // takes keys 32 h + 16 u + 4 g + e (e = 0..3), 16 dims each, as two pieces.
+  // (db varies fastest, so one 64-slot copy instruction reads 16 keys x 64
+  // contiguous bytes, as for K, rather than 32 keys x 32 bytes.)
+  static_assert(DB % 2 == 0, "a copy instruction covers two dim blocks");
   __device__ static void v_slot(int j, int& row, int& piece) {
     const int i = j >> 5, q = j & 31;
-    const int u = i & 1, db = (i >> 1) % DB, h = (i >> 1) / DB;
+    const int db = i % DB, u = (i / DB) & 1, h = i / (2 * DB);
     row = h * 32 + u * 16 + 4 * (q >> 3) + ((q & 7) >> 1);
     piece = 2 * db + (q & 1);
   }
@@ -132,9 +135,9 @@ struct TileLayout<__bf16, D> {
   // lane (r, g) is tile key 32 h + 4 g + (e < 4 ? e : 12 + e)
   __device__ static Frag<__bf16> vt_frag(const __bf16* vs, int h, int db, int lane) {
     typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    const __bf16* p = vs + (h * DB + db) * 512 + lane * 4;
+    const __bf16* p = vs + (2 * h * DB + db) * 256 + lane * 4;
     const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 256));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + DB * 256));
     Frag<__bf16> f;
     f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return f;
