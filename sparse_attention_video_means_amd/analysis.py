@@ -26,6 +26,15 @@ the maximum) and the map MSE of the method at one density:
 
     python -m sparse_attention_video_means_amd.analysis --workload slice \\
         --sweep-cq 25,50,100,200,300 --densities 0.1
+
+With ``--turbo`` each setting C_q:C_k:rho (fewer centroids and a lower density
+budget, the trade of §5.1's SVG-EAR-turbo) runs the whole routed path as the
+benchmark does, timed per stage over a few passes, and reports its map MSE,
+normaliser change and exact density next to top-p with compensation at the
+same budget:
+
+    python -m sparse_attention_video_means_amd.analysis --workload wan22 \\
+        --turbo 100:500:0.1,50:250:0.1,50:250:0.05
 """
 from __future__ import annotations
 
@@ -117,6 +126,71 @@ def sweep_cq(workload: str, cqs, rho: float, heads: int | None = None, n: int | 
     return out
 
 
+def turbo(workload: str, settings, heads: int | None = None, n: int | None = None,
+          reps: int = 3):
+    base = synth.WORKLOADS[workload]
+    if heads:
+        base = base.with_(heads=heads)
+    if n:
+        base = base.with_(n=n)
+    dev = "cuda"
+    q, k, v = synth.make_qkv(base, threads=16)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    dtype = torch.bfloat16 if base.dtype == "bf16" else torch.float32
+    total = float(base.heads) * base.n * base.n
+    out = []
+    for cq, ck, rho in settings:
+        wl = base.with_(cq=cq, ck=ck, rho=rho)
+        iq = synth.kmeans_init(q, cq, wl.seed, 0).to(dev)
+        ik = synth.kmeans_init(k, ck, wl.seed, 1).to(dev)
+        ra = svgear.RoutedAttention(wl.heads, wl.n, wl.d, cq, ck, wl.budget, wl.iters, dtype, dev)
+        ra(qd, kd, vd, iq, ik)
+        stages = {s: 0.0 for s in ra.STAGES}
+        events = []
+        for _ in range(reps):
+            ra(qd, kd, vd, iq, ik, stage_events=True)
+            events.append(ra._events)
+        torch.cuda.synchronize()
+        for ev in events:
+            for i, name in enumerate(ra.STAGES):
+                stages[name] += ev[2 * i].elapsed_time(ev[2 * i + 1]) / reps
+        core = sum(v for name, v in stages.items() if name != "unpermute")
+        qn = (ra.q_off[:, 1:] - ra.q_off[:, :-1]).double()
+        line = {"workload": f"{wl.name}: H={wl.heads} N={wl.n} d={wl.d} {wl.dtype} "
+                            f"iters={wl.iters}",
+                "cq": cq, "ck": ck, "rho": rho, "budget_keys": wl.budget,
+                "core_ms": core, "stages_ms": stages}
+        scores = svgear.svgear_block_scores(ra.q_bar, ra.k_bar, ra.k_off, ra.scale)
+        for name, mask in (("error_aware_comp", ra.sel_mask),
+                           ("topp_comp", svgear.svgear_route(scores, ra.k_off, wl.budget)[0])):
+            err, zf, zs = svgear.svgear_map_error(ra.qp, ra.kp, ra.q_off, ra.k_off, ra.k_bar, mask,
+                                                  ra.scale, compensate=True)
+            keys = mask.to(torch.int64).mul(
+                (ra.k_off[:, 1:] - ra.k_off[:, :-1]).to(torch.int64)[:, None, :]).sum(2)
+            line[name] = {"mse": float(err.double().sum()) / total,
+                          "normaliser_change": float((zs.double() / zf.double() - 1).abs().mean()),
+                          "density": float((qn * keys.double()).sum()) / total}
+        out.append(line)
+        print(json.dumps(line), flush=True)
+        del ra
+        torch.cuda.empty_cache()
+    return out
+
+
+def parse_turbo(text: str):
+    """'C_q:C_k:rho,...' -> [(C_q, C_k, rho), ...]; raises ValueError on a malformed item."""
+    settings = []
+    for item in text.split(","):
+        parts = item.split(":")
+        if len(parts) != 3:
+            raise ValueError(f"turbo setting {item!r} is not C_q:C_k:rho")
+        cq, ck, rho = int(parts[0]), int(parts[1]), float(parts[2])
+        if cq < 1 or ck < 1 or not 0.0 <= rho <= 1.0:
+            raise ValueError(f"turbo setting {item!r} is out of range")
+        settings.append((cq, ck, rho))
+    return settings
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", default="slice", choices=sorted(synth.WORKLOADS))
@@ -125,12 +199,17 @@ def main(argv=None):
     ap.add_argument("--n", type=int, default=None, help="override the token count")
     ap.add_argument("--sweep-cq", default=None,
                     help="comma-separated query-cluster counts (uses the first density)")
+    ap.add_argument("--turbo", default=None,
+                    help="comma-separated C_q:C_k:rho settings, each timed on the whole path")
     args = ap.parse_args(argv)
+    settings = parse_turbo(args.turbo) if args.turbo else None
     if not torch.cuda.is_available():
         print("the analysis runs on the GPU kernels; no GPU is visible", file=sys.stderr)
         return 2
     densities = [float(x) for x in args.densities.split(",")]
-    if args.sweep_cq:
+    if settings:
+        turbo(args.workload, settings, args.heads, args.n)
+    elif args.sweep_cq:
         sweep_cq(args.workload, [int(x) for x in args.sweep_cq.split(",")], densities[0],
                  args.heads, args.n)
     else:
