@@ -37,6 +37,9 @@ def parse():
                          "budget of exact entries per head")
     ap.add_argument("--probe", choices=("weight", "value"), default="weight",
                     help="block errors from the weight gap or from the value-aware gap")
+    ap.add_argument("--cq", type=int, default=None, help="override the workload's query clusters")
+    ap.add_argument("--ck", type=int, default=None, help="override the workload's key clusters")
+    ap.add_argument("--rho", type=float, default=None, help="override the workload's density")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -132,6 +135,9 @@ def main():
     from sparse_attention_video_means_amd import svgear, synth
 
     wl = synth.WORKLOADS[args.workload]
+    over = {k: v for k, v in (("cq", args.cq), ("ck", args.ck), ("rho", args.rho)) if v is not None}
+    if over:
+        wl = wl.with_(**over)
     print(f"[bench] generating {wl.name}: H={wl.heads} N={wl.n} d={wl.d} {wl.dtype}",
           file=sys.stderr, flush=True)
     t0 = time.time()
