@@ -349,7 +349,9 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
           mp[cb] = M;
         }
         if (g == 0 && cok[cb]) {
-          float* o = rec + ((size_t(h) * maxu + cur.u) * Cq + cidx[cb]) * RS;
+          // records are centroid-major ([h][c][unit]), so that the finalize
+          // pass reads each centroid's units contiguously
+          float* o = rec + ((size_t(h) * Cq + cidx[cb]) * maxu + cur.u) * RS;
           o[0] = st[cb] + mp[cb];  // absolute base-2 reference of this unit
           o[1] = Z[cb];
           o[2] = E[cb];
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(256) void probe_finalize_kernel(int Cq, int Ck, int
   const int32_t* up = unit_prefix + size_t(h) * (Ck + 1);
   const int32_t* ko = koff + size_t(h) * (Ck + 1);
   const int nu = up[Ck];
-  auto R = [&](int u, int k) { return rec[((size_t(h) * maxu + u) * Cq + c) * RS + k]; };
+  auto R = [&](int u, int k) { return rec[((size_t(h) * Cq + c) * maxu + u) * RS + k]; };
 
   float mx = -__builtin_inff();
   for (int u = tid; u < nu; u += 256) mx = fmaxf(mx, R(u, 0));
