@@ -245,17 +245,36 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
       T* dlo = kl + srow * LDR + sq * QD;
 #pragma unroll
       for (int i = 0; i < RAW; ++i) {
-        const T* el = reinterpret_cast<const T*>(&raw[i]);
         constexpr int E8 = 16 / sizeof(T);
-        T out[E8], rem[E8];
+        if constexpr (kSplit) {
+          // bf16 pairs: unpack, subtract kbar, round to the high part and the
+          // remainder two at a time (the same round-to-nearest-even values as
+          // element by element)
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+          uint32_t hi4[4], lo4[4];
 #pragma unroll
-        for (int e = 0; e < E8; ++e) {
-          const float dlt = ok ? to_f32(el[e]) - kb[i * E8 + e] : 0.f;
-          out[e] = from_f32<T>(dlt);
-          rem[e] = from_f32<T>(dlt - to_f32(out[e]));
+          for (int w2 = 0; w2 < 4; ++w2) {
+            const uint32_t wd = (&raw[i].x)[w2];
+            const f2 x = {__uint_as_float(wd << 16), __uint_as_float(wd & 0xffff0000u)};
+            const f2 dl = x - f2{kb[i * E8 + 2 * w2], kb[i * E8 + 2 * w2 + 1]};
+            const b2 hb = __builtin_convertvector(dl, b2);
+            const uint32_t hw = __builtin_bit_cast(uint32_t, hb);
+            const f2 hf = {__uint_as_float(hw << 16), __uint_as_float(hw & 0xffff0000u)};
+            hi4[w2] = hw;
+            lo4[w2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(dl - hf, b2));
+          }
+          const uint4 hv = ok ? make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]) : make_uint4(0, 0, 0, 0);
+          const uint4 lv = ok ? make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]) : make_uint4(0, 0, 0, 0);
+          *reinterpret_cast<uint4*>(dst + i * E8) = hv;
+          *reinterpret_cast<uint4*>(dlo + i * E8) = lv;
+        } else {
+          const T* el = reinterpret_cast<const T*>(&raw[i]);
+          T out[E8];
+#pragma unroll
+          for (int e = 0; e < E8; ++e) out[e] = ok ? el[e] - kb[i * E8 + e] : 0.f;
+          *reinterpret_cast<uint4*>(dst + i * E8) = *reinterpret_cast<const uint4*>(out);
         }
-        *reinterpret_cast<uint4*>(dst + i * E8) = *reinterpret_cast<const uint4*>(out);
-        if (kSplit) *reinterpret_cast<uint4*>(dlo + i * E8) = *reinterpret_cast<const uint4*>(rem);
       }
       if (VALUE && sq == 0) vs[srow] = vraw;
     }
