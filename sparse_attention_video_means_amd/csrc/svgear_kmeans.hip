@@ -8,8 +8,8 @@
 // input element type and ||round(mu)||^2 in f32, so one chain of MFMAs seeded
 // with the norms yields ||mu||^2 - 2 x.mu directly. Each lane keeps a running
 // (distance, index) minimum over the centroids it sees in increasing index
-// order; four lanes share a row and are merged with the lower index winning
-// ties. The block then ranks its rows among equal labels (for the counting
+// order, two candidates at a time; four lanes share a row and are merged with
+// the lower index winning ties. The block then ranks its rows among equal labels (for the counting
 // sort that follows) without atomics.
 #include "svgear_common.hpp"
 #include "svgear_internal.hpp"
@@ -94,9 +94,16 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X,
         f32x4 acc = init;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) mma(acc, a[kc], xb[tb][kc]);
+        // two candidates per step: the new minimum of (best, a, b) in one
+        // instruction, then its index; ties keep the lower index (the running
+        // best, then a before b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (acc[i] < best[tb]) { best[tb] = acc[i]; bidx[tb] = c0 + i; }
+        for (int i = 0; i < 4; i += 2) {
+          const float nb = __builtin_fminf(best[tb], __builtin_fminf(acc[i], acc[i + 1]));
+          const bool keep = nb == best[tb];
+          const int cand = (nb == acc[i]) ? c0 + i : c0 + i + 1;
+          bidx[tb] = keep ? bidx[tb] : cand;
+          best[tb] = nb;
         }
       }
     }
