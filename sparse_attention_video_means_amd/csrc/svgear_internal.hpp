@@ -25,7 +25,7 @@ inline int max_units(int Nk, int Ck) { return ceil_div(Nk, kProbeUnit) + Ck; }
 // Workspace carve-up for a counting sort + segment means over H heads.
 struct SortWs {
   int32_t* rank;          // [H][N]
-  int32_t* hist;          // [H][C][tiles] -> exclusive bases after the scan
+  int32_t* hist;          // [H][tiles][C] -> exclusive bases after the scan
   int32_t* chunk_prefix;  // [H][C+1]
   int32_t* sizes;         // [H][C]
   float* partial;         // [H][ntensors][max_chunks][d]
@@ -36,7 +36,7 @@ SortWs sort_ws_carve(void* ws, int H, int N, int d, int C, int ntensors);
 // sort.hip
 hipError_t launch_label_rank(const int32_t* labels, int H, int N, int C, int32_t* rank,
                              int32_t* hist, hipStream_t s);
-// hist [H][C][tiles] becomes every tile's exclusive prefix within its cluster.
+// hist [H][tiles][C] becomes every tile's exclusive prefix within its cluster.
 hipError_t launch_sort_scan(int H, int N, int C, int32_t* hist, int32_t* sizes, int32_t* offsets,
                             int32_t* counts, int32_t* chunk_prefix, hipStream_t s);
 hipError_t launch_scatter(const int32_t* labels, const int32_t* rank, const int32_t* hist,

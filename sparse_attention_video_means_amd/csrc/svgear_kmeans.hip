@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X,
   const int rk = tile_rank(my, valid, C, wave_hist);
   if (valid) rank[size_t(h) * N + n] = rk;
   for (int c = tid; c < C; c += 256)
-    hist[(size_t(h) * C + c) * tiles + t] =
+    hist[(size_t(h) * tiles + t) * C + c] =
         wave_hist[c] + wave_hist[C + c] + wave_hist[2 * C + c] + wave_hist[3 * C + c];
 }
 

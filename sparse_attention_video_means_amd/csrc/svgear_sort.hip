@@ -5,9 +5,10 @@
 // Pipeline for one tensor family, all heads at once:
 //   label_rank  : per 256-row tile, stable rank of each row among equal labels
 //                 of the tile (wave ballots, no atomics) + tile histogram.
-//   sort_scan   : per head, exclusive scan of the [cluster][tile] histogram in
-//                 cluster-major order -> every tile's base slot per cluster,
-//                 cluster offsets and the per-cluster chunk list.
+//   sort_scan   : per head, exclusive scan over tiles of the [tile][cluster]
+//                 histogram (each tile writes one contiguous row) -> every
+//                 tile's base slot per cluster, cluster offsets and the
+//                 per-cluster chunk list.
 //   scatter     : perm[base + rank] = row (stable by construction).
 //   segsum      : per chunk of <= 1024 slots of one cluster, gather the rows
 //                 (optionally storing the permuted copy) and sum them in f32 in a
@@ -58,28 +59,55 @@ __global__ __launch_bounds__(256) void label_rank_kernel(const int32_t* __restri
   const int r = tile_rank(label, valid, C, wave_hist);
   if (valid) rank[size_t(h) * N + n] = r;
   for (int c = tid; c < C; c += 256)
-    hist[(size_t(h) * C + c) * tiles + t] =
+    hist[(size_t(h) * tiles + t) * C + c] =
         wave_hist[c] + wave_hist[C + c] + wave_hist[2 * C + c] + wave_hist[3 * C + c];
 }
 
-// Per (head, cluster): exclusive prefix of the cluster's tile counts, in
-// place, and the cluster's size. One wavefront per cluster row.
-__global__ __launch_bounds__(256) void tile_prefix_kernel(int C, int tiles,
-                                                          int32_t* __restrict__ hist,
-                                                          int32_t* __restrict__ sizes) {
-  const int h = blockIdx.y, lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (c >= C) return;
-  int32_t* row = hist + (size_t(h) * C + c) * tiles;
+// Per (head, 64 clusters): exclusive prefix over tiles of the cluster counts,
+// in place, and the cluster sizes. Each of the block's wavefronts sums a
+// contiguous run of tiles (lane = cluster, so every read covers 64 adjacent
+// counts of one tile), the runs' totals are combined in run order through LDS,
+// and a second pass over the run writes the prefixes.
+constexpr int kPrefixWaves = 16;
+__global__ __launch_bounds__(64 * kPrefixWaves) void tile_prefix_kernel(int C, int tiles,
+                                                                       int32_t* __restrict__ hist,
+                                                                       int32_t* __restrict__ sizes) {
+  __shared__ int run_sum[kPrefixWaves][64];
+  const int h = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 64 + lane;
+  const bool ok = c < C;
+  const int per = (tiles + kPrefixWaves - 1) / kPrefixWaves;
+  const int t0 = min(tiles, w * per), t1 = min(tiles, t0 + per);
+  int32_t* col = hist + size_t(h) * tiles * C + (ok ? c : 0);
+  // reads go out kBatch at a time, so a run costs a few memory round trips
+  constexpr int kBatch = 16;
+  int sum = 0;
+  if (ok)
+    for (int tb = t0; tb < t1; tb += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = (tb + i < t1) ? col[size_t(tb + i) * C] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) sum += v[i];
+    }
+  run_sum[w][lane] = sum;
+  __syncthreads();
   int carry = 0;
-  for (int t0 = 0; t0 < tiles; t0 += 64) {
-    const int t = t0 + lane;
-    const int v = t < tiles ? row[t] : 0;
-    const int inc = wave_inclusive_scan(v);
-    if (t < tiles) row[t] = carry + inc - v;
-    carry += __shfl(inc, 63, 64);
+  for (int i = 0; i < w; ++i) carry += run_sum[i][lane];
+  if (ok) {
+    for (int tb = t0; tb < t1; tb += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = (tb + i < t1) ? col[size_t(tb + i) * C] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (tb + i < t1) {
+          col[size_t(tb + i) * C] = carry;
+          carry += v[i];
+        }
+    }
+    if (w == kPrefixWaves - 1) sizes[size_t(h) * C + c] = carry;
   }
-  if (lane == 0) sizes[size_t(h) * C + c] = carry;
 }
 
 // Per head: cluster offsets and the chunk list of the segment sums.
@@ -117,7 +145,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int n = t * kTile + threadIdx.x;
   if (n >= N) return;
   const int lab = min(max(labels[size_t(h) * N + n], 0), C - 1);
-  const int p = offsets[size_t(h) * (C + 1) + lab] + tpre[(size_t(h) * C + lab) * tiles + t] +
+  const int p = offsets[size_t(h) * (C + 1) + lab] + tpre[(size_t(h) * tiles + t) * C + lab] +
                 rank[size_t(h) * N + n];
   perm[size_t(h) * N + p] = n;
 }
@@ -267,7 +295,8 @@ hipError_t launch_label_rank(const int32_t* labels, int H, int N, int C, int32_t
 
 hipError_t launch_sort_scan(int H, int N, int C, int32_t* hist, int32_t* sizes, int32_t* offsets,
                             int32_t* counts, int32_t* chunk_prefix, hipStream_t s) {
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(ceil_div(C, 4), H), dim3(256), 0, s, C,
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(ceil_div(C, 64), H), dim3(64 * kPrefixWaves), 0, s,
+                     C,
                      sort_tiles(N), hist, sizes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
