@@ -4,7 +4,8 @@
 One step = one pass of the whole path over one attention layer of the
 Wan2.2-shaped workload (40 heads x 75,600 tokens x d=128, bf16, C_q=100,
 C_k=500, density 0.10, 10 Lloyd iterations): cluster(Q), cluster(K),
-permute(Q), permute(K, V), probe, route, attend, unpermute. Inputs are
+permute(Q), permute(K, V), probe, route, attend with the unpermutation in its
+epilogue. Inputs are
 generated on the host, copied to the GPU, and resident in HBM before the
 timed region starts.
 

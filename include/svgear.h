@@ -20,6 +20,8 @@
  *   svgear_row_spread    squared distance of every permuted row from its cluster mean
  *   svgear_attend    exact selected blocks + centroid compensation (§4.1, §4.3)
  *   svgear_unpermute inverse permutation of the output rows        (§3.1)
+ *   svgear_attend_unpermute  svgear_attend writing each output row at its
+ *                    query's original position (§3.1, §4.1, §4.3)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -281,6 +283,26 @@ svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int C
                             const float* k_centroids, const float* v_centroids,
                             const uint8_t* sel_mask, void* Op, void* ws, size_t ws_bytes,
                             svgear_stream_t s);
+
+/*
+ * svgear_attend followed by svgear_unpermute in one pass (paper §3.1: the
+ * output of the permuted layout is mapped back to the original token order;
+ * §4.1, §4.3: the attention itself). Arguments as svgear_attend, except
+ *   q_perm [H][Nq] int32: the query permutation (q_perm[h][p] is the original
+ *          row of permuted row p; a permutation of 0..Nq-1 per head);
+ *   O      [H][Nq][d] dt out, in the original query order: O[h][q_perm[h][p]]
+ *          is the result for permuted query p, bitwise what svgear_attend then
+ *          svgear_unpermute write. Rows whose q_perm value lies outside
+ *          [0, Nq) are not written. O must not alias Qp.
+ * Errors as svgear_attend; a NULL q_perm is SVGEAR_ERR_INVALID_ARG.
+ */
+svgear_status svgear_attend_unpermute(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq,
+                                      int Ck, float scale, const void* Qp, const void* Kp,
+                                      const void* Vp, const int32_t* q_offsets,
+                                      const int32_t* k_offsets, const float* k_centroids,
+                                      const float* v_centroids, const uint8_t* sel_mask,
+                                      const int32_t* q_perm, void* O, void* ws, size_t ws_bytes,
+                                      svgear_stream_t s);
 
 /*
  * Inverse permutation of output rows: X[h][perm[h][p]] = Xp[h][p] (paper §3.1).

@@ -6,5 +6,5 @@ ABI, declared in ``include/svgear.h``); ``svgear`` is its ctypes binding and
 """
 from .svgear import (  # noqa: F401
     SvgearError, budget_keys, lib, routed_attention, svgear_attend, svgear_cluster,
-    svgear_permute, svgear_probe, svgear_route, svgear_unpermute,
+    svgear_attend_unpermute, svgear_permute, svgear_probe, svgear_route, svgear_unpermute,
 )

@@ -63,6 +63,29 @@ ClusterWs cluster_ws_carve(void* ws, int eb, int H, int N, int d, int C, int nt 
     if ((expr) != hipSuccess) return SVGEAR_ERR_HIP;       \
   } while (0)
 
+svgear_status attend_common(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
+                            float scale, const void* Qp, const void* Kp, const void* Vp,
+                            const int32_t* q_offsets, const int32_t* k_offsets,
+                            const float* k_centroids, const float* v_centroids,
+                            const uint8_t* sel_mask, const int32_t* q_perm, void* Op, void* ws,
+                            size_t ws_bytes, svgear_stream_t s) {
+  svgear_status st = check_shape(dt, H, Nq, d, Cq);
+  if (st != SVGEAR_OK) return st;
+  st = check_shape(dt, H, Nk, d, Ck);
+  if (st != SVGEAR_OK) return st;
+  if (!(scale > 0.f) || !Qp || !Kp || !Vp || !q_offsets || !k_offsets || !k_centroids ||
+      !v_centroids || !sel_mask || !Op)
+    return SVGEAR_ERR_INVALID_ARG;
+  // the tile copies address one head's K or V with 32-bit byte offsets
+  if (size_t(Nk) * d * elem_bytes(dt) >= (size_t(1) << 32)) return SVGEAR_ERR_INVALID_ARG;
+  const size_t need = attend_ws_bytes(elem_bytes(dt), H, Ck, d);
+  if (need > 0 && (!ws || ws_bytes < need)) return SVGEAR_ERR_WORKSPACE;
+  SVG_TRY(launch_attend(elem_bytes(dt), H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets,
+                        k_offsets, k_centroids, v_centroids, sel_mask, q_perm, Op, ws,
+                        as_stream(s)));
+  return SVGEAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -285,20 +308,20 @@ svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int C
                             const float* k_centroids, const float* v_centroids,
                             const uint8_t* sel_mask, void* Op, void* ws, size_t ws_bytes,
                             svgear_stream_t s) {
-  svgear_status st = check_shape(dt, H, Nq, d, Cq);
-  if (st != SVGEAR_OK) return st;
-  st = check_shape(dt, H, Nk, d, Ck);
-  if (st != SVGEAR_OK) return st;
-  if (!(scale > 0.f) || !Qp || !Kp || !Vp || !q_offsets || !k_offsets || !k_centroids ||
-      !v_centroids || !sel_mask || !Op)
-    return SVGEAR_ERR_INVALID_ARG;
-  // the tile copies address one head's K or V with 32-bit byte offsets
-  if (size_t(Nk) * d * elem_bytes(dt) >= (size_t(1) << 32)) return SVGEAR_ERR_INVALID_ARG;
-  const size_t need = attend_ws_bytes(elem_bytes(dt), H, Ck, d);
-  if (need > 0 && (!ws || ws_bytes < need)) return SVGEAR_ERR_WORKSPACE;
-  SVG_TRY(launch_attend(elem_bytes(dt), H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets,
-                        k_offsets, k_centroids, v_centroids, sel_mask, Op, ws, as_stream(s)));
-  return SVGEAR_OK;
+  return attend_common(dt, H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets, k_offsets,
+                       k_centroids, v_centroids, sel_mask, nullptr, Op, ws, ws_bytes, s);
+}
+
+svgear_status svgear_attend_unpermute(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq,
+                                      int Ck, float scale, const void* Qp, const void* Kp,
+                                      const void* Vp, const int32_t* q_offsets,
+                                      const int32_t* k_offsets, const float* k_centroids,
+                                      const float* v_centroids, const uint8_t* sel_mask,
+                                      const int32_t* q_perm, void* O, void* ws, size_t ws_bytes,
+                                      svgear_stream_t s) {
+  if (!q_perm || O == Qp) return SVGEAR_ERR_INVALID_ARG;
+  return attend_common(dt, H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets, k_offsets,
+                       k_centroids, v_centroids, sel_mask, q_perm, O, ws, ws_bytes, s);
 }
 
 svgear_status svgear_unpermute(svgear_dtype dt, int H, int N, int d, const int32_t* perm,

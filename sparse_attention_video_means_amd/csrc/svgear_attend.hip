@@ -228,7 +228,7 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
     const int32_t* __restrict__ qoff, const int32_t* __restrict__ koff,
     const T* __restrict__ kcen, const T* __restrict__ vcen, const uint8_t* __restrict__ mask,
     int H, int Nq, int Nk, int Cq, int Ck, float sl2, int per_head, int span,
-    T* __restrict__ Op) {
+    const int32_t* __restrict__ qperm, T* __restrict__ Op) {
   using L = TileLayout<T, D>;
   constexpr int QB = AttCfg<T>::QB;
   constexpr int NW = AttCfg<T>::NW;
@@ -599,11 +599,15 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
 
   if (!active) return;
   T* Oh = Op + size_t(h) * Nq * D;
+  // with a query permutation, row qi of the permuted order is written to the
+  // query's original row (rows outside [0, Nq) are dropped)
+  const int32_t* ph = qperm ? qperm + size_t(h) * Nq : nullptr;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float inv = 1.f / (kOnesSum ? lacc[qb][0] : quad_sum(lsum[qb]));
-    const int qi = qw + qb * 16 + r;
-    if (qi < q1) {
+    const int qp = qw + qb * 16 + r;
+    const int qi = (ph && qp < q1) ? ph[qp] : qp;
+    if (qp < q1 && unsigned(qi) < unsigned(Nq)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         float v[4];
@@ -633,8 +637,8 @@ size_t attend_ws_bytes(int elem_bytes, int H, int Ck, int d) {
 template <typename T, int D>
 static void attend_t(int H, int Nq, int Nk, int Cq, int Ck, float sl2, const void* Qp,
                      const void* Kp, const void* Vp, const int32_t* qoff, const int32_t* koff,
-                     const void* kc, const void* vc, const uint8_t* mask, void* Op,
-                     hipStream_t s) {
+                     const void* kc, const void* vc, const uint8_t* mask,
+                     const int32_t* qperm, void* Op, hipStream_t s) {
   constexpr int BM = 16 * AttCfg<T>::NW * AttCfg<T>::QB;
   const int per_head = ceil_div(Nq, BM) + Cq;  // upper bound on query tiles per head
   const int span = ceil_div(H * per_head, kXcds);
@@ -643,14 +647,14 @@ static void attend_t(int H, int Nq, int Nk, int Cq, int Ck, float sl2, const voi
                      static_cast<const T*>(Qp), static_cast<const T*>(Kp),
                      static_cast<const T*>(Vp), qoff, koff, static_cast<const T*>(kc),
                      static_cast<const T*>(vc), mask, H, Nq, Nk, Cq, Ck, sl2, per_head, span,
-                     static_cast<T*>(Op));
+                     qperm, static_cast<T*>(Op));
 }
 
 hipError_t launch_attend(int elem_bytes, int H, int Nq, int Nk, int d, int Cq, int Ck,
                          float scale, const void* Qp, const void* Kp, const void* Vp,
                          const int32_t* qoff, const int32_t* koff, const float* kc,
-                         const float* vc, const uint8_t* mask, void* Op, void* ws,
-                         hipStream_t s) {
+                         const float* vc, const uint8_t* mask, const int32_t* qperm, void* Op,
+                         void* ws, hipStream_t s) {
   const float sl2 = scale * 1.44269504088896340736f;
   if (elem_bytes == 2) {
     const size_t n = size_t(H) * Ck * d;
@@ -658,11 +662,11 @@ hipError_t launch_attend(int elem_bytes, int H, int Nq, int Nk, int d, int Cq, i
     __bf16* rv = reinterpret_cast<__bf16*>(static_cast<char*>(ws) + align256(2 * n));
     hipLaunchKernelGGL(round_rows_kernel<__bf16>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
                        n, kc, vc, rk, rv);
-    if (d == 128) attend_t<__bf16, 128>(H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp, qoff, koff, rk, rv, mask, Op, s);
-    else attend_t<__bf16, 64>(H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp, qoff, koff, rk, rv, mask, Op, s);
+    if (d == 128) attend_t<__bf16, 128>(H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp, qoff, koff, rk, rv, mask, qperm, Op, s);
+    else attend_t<__bf16, 64>(H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp, qoff, koff, rk, rv, mask, qperm, Op, s);
   } else {
-    if (d == 128) attend_t<float, 128>(H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp, qoff, koff, kc, vc, mask, Op, s);
-    else attend_t<float, 64>(H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp, qoff, koff, kc, vc, mask, Op, s);
+    if (d == 128) attend_t<float, 128>(H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp, qoff, koff, kc, vc, mask, qperm, Op, s);
+    else attend_t<float, 64>(H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp, qoff, koff, kc, vc, mask, qperm, Op, s);
   }
   return hipGetLastError();
 }

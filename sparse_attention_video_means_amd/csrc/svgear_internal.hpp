@@ -87,8 +87,8 @@ hipError_t launch_route_global(int H, int Cq, int Ck, const float* ratio, const 
 hipError_t launch_attend(int elem_bytes, int H, int Nq, int Nk, int d, int Cq, int Ck,
                          float scale, const void* Qp, const void* Kp, const void* Vp,
                          const int32_t* qoff, const int32_t* koff, const float* kc,
-                         const float* vc, const uint8_t* mask, void* Op, void* ws,
-                         hipStream_t s);
+                         const float* vc, const uint8_t* mask, const int32_t* qperm, void* Op,
+                         void* ws, hipStream_t s);
 size_t attend_ws_bytes(int elem_bytes, int H, int Ck, int d);
 
 // analysis.hip

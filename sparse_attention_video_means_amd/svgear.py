@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
             "svgear_attend_workspace": (sz, [i32, i32, i32, i32]),
             "svgear_attend": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp, sz, vp]),
+            "svgear_attend_unpermute": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
+                                              vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "svgear_unpermute": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "svgear_block_scores": (i32, [i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]),
             "svgear_map_error_workspace": (sz, [i32, i32, i32]),
@@ -84,7 +86,8 @@ EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
            "svgear_cluster_permute", "svgear_probe_workspace", "svgear_probe",
            "svgear_probe_values_workspace", "svgear_probe_values",
            "svgear_route", "svgear_route_global_workspace", "svgear_route_global",
-           "svgear_attend_workspace", "svgear_attend", "svgear_unpermute",
+           "svgear_attend_workspace", "svgear_attend", "svgear_attend_unpermute",
+           "svgear_unpermute",
            "svgear_block_scores", "svgear_map_error_workspace", "svgear_map_error",
            "svgear_row_spread")
 
@@ -319,6 +322,33 @@ def svgear_attend(qp, kp, vp, q_offsets, k_offsets, k_centroids, v_centroids, se
     return op
 
 
+def svgear_attend_unpermute(qp, kp, vp, q_offsets, k_offsets, k_centroids, v_centroids,
+                            sel_mask, q_perm, scale: float, out=None):
+    """svgear_attend with every output row written at its query's original
+    position (q_perm [H, Nq] int32, permuted row -> original row); returns O."""
+    _need(qp, "qp")
+    H, Nq, d = qp.shape
+    Nk = kp.shape[1]
+    Cq, Ck = q_offsets.shape[1] - 1, k_offsets.shape[1] - 1
+    _need(kp, "kp", qp.dtype, (H, Nk, d))
+    _need(vp, "vp", qp.dtype, (H, Nk, d))
+    _need(q_offsets, "q_offsets", torch.int32, (H, Cq + 1))
+    _need(k_offsets, "k_offsets", torch.int32, (H, Ck + 1))
+    _need(k_centroids, "k_centroids", torch.float32, (H, Ck, d))
+    _need(v_centroids, "v_centroids", torch.float32, (H, Ck, d))
+    _need(sel_mask, "sel_mask", torch.uint8, (H, Cq, Ck))
+    _need(q_perm, "q_perm", torch.int32, (H, Nq))
+    o = torch.empty_like(qp) if out is None else out
+    _need(o, "out", qp.dtype, qp.shape)
+    L = lib()
+    ws = _ws(L.svgear_attend_workspace(_dt(qp), H, Ck, d), qp.device)
+    _check("svgear_attend_unpermute", L.svgear_attend_unpermute(
+        _dt(qp), H, Nq, Nk, d, Cq, Ck, float(scale), _ptr(qp), _ptr(kp), _ptr(vp),
+        _ptr(q_offsets), _ptr(k_offsets), _ptr(k_centroids), _ptr(v_centroids), _ptr(sel_mask),
+        _ptr(q_perm), _ptr(o), _ptr(ws), ws.numel(), _stream()))
+    return o
+
+
 def svgear_unpermute(xp, perm, out=None):
     """X[perm[p]] = Xp[p] per head."""
     _need(xp, "xp")
@@ -344,7 +374,9 @@ class RoutedAttention:
     stage (``last_stage_ms()`` reads them after a synchronisation).
     """
 
-    STAGES = ("cluster_permute_q", "cluster_permute_kv", "probe", "route", "attend", "unpermute")
+    # "attend" writes every output row at its query's original position (the
+    # unpermutation runs in the attention kernel's epilogue)
+    STAGES = ("cluster_permute_q", "cluster_permute_kv", "probe", "route", "attend")
 
     def __init__(self, H, N, d, cq, ck, budget, iters, dtype=torch.bfloat16, device="cuda",
                  nk=None, scale=None, routing="cluster", probe="weight"):
@@ -370,7 +402,7 @@ class RoutedAttention:
         self.ratio, self.log_norm = e(H, cq, ck, dt=torch.float32), e(H, cq, dt=torch.float32)
         self.sel_mask = e(H, cq, ck, dt=torch.uint8)
         self.sel_list, self.sel_count, self.sel_keys = e(H, cq, ck), e(H, cq), e(H, cq)
-        self.op, self.o = e(H, nq, d, dt=dtype), e(H, nq, d, dt=dtype)
+        self.o = e(H, nq, d, dt=dtype)
         self.used_entries = e(H, dt=torch.int64)
         L = lib()
         wsz = max(L.svgear_route_global_workspace(H, cq, ck) if routing == "global" else 0,
@@ -428,15 +460,11 @@ class RoutedAttention:
                 _ptr(self.sel_mask), _ptr(self.sel_list), _ptr(self.sel_count),
                 _ptr(self.sel_keys), _ptr(self.used_entries), ws, wn, s))
         mark(7); mark(8)
-        _check("svgear_attend", L.svgear_attend(dt, H, nq, nk, d, cq, ck, self.scale,
-                                                _ptr(self.qp), _ptr(self.kp), _ptr(self.vp),
-                                                _ptr(self.q_off), _ptr(self.k_off),
-                                                _ptr(self.k_bar), _ptr(self.v_bar),
-                                                _ptr(self.sel_mask), _ptr(self.op), ws, wn, s))
-        mark(9); mark(10)
-        _check("svgear_unpermute", L.svgear_unpermute(dt, H, nq, d, _ptr(self.perm_q),
-                                                      _ptr(self.op), _ptr(self.o), s))
-        mark(11)
+        _check("svgear_attend_unpermute", L.svgear_attend_unpermute(
+            dt, H, nq, nk, d, cq, ck, self.scale, _ptr(self.qp), _ptr(self.kp), _ptr(self.vp),
+            _ptr(self.q_off), _ptr(self.k_off), _ptr(self.k_bar), _ptr(self.v_bar),
+            _ptr(self.sel_mask), _ptr(self.perm_q), _ptr(self.o), ws, wn, s))
+        mark(9)
         self._events = ev
         return self.o
 

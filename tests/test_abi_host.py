@@ -128,5 +128,16 @@ def test_argument_errors_return_before_any_launch(L):
     assert L.svgear_attend_workspace(0, 2, 50, 128) == 0
     assert L.svgear_attend(1, 1, 100, 100, 64, 4, 11, 0.1, fake, fake, fake, fake, fake, fake,
                            fake, fake, fake, null, 0, null) == 3
+    # attend with the unpermutation: q_perm required, O must not alias Qp, and the
+    # same workspace rule as attend
+    other = ctypes.c_void_p(fake.value + 4096)
+    assert L.svgear_attend_unpermute(1, 1, 100, 100, 64, 4, 11, 0.1, fake, fake, fake, fake,
+                                     fake, fake, fake, fake, null, other, fake, 1 << 30,
+                                     null) == 1
+    assert L.svgear_attend_unpermute(1, 1, 100, 100, 64, 4, 11, 0.1, fake, fake, fake, fake,
+                                     fake, fake, fake, fake, fake, fake, fake, 1 << 30,
+                                     null) == 1
+    assert L.svgear_attend_unpermute(1, 1, 100, 100, 64, 4, 11, 0.1, fake, fake, fake, fake,
+                                     fake, fake, fake, fake, fake, other, null, 0, null) == 3
     # unpermute: aliasing
     assert L.svgear_unpermute(1, 1, 100, 64, fake, fake, fake, null) == 1

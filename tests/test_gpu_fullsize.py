@@ -13,7 +13,8 @@ are sampled on two heads (the first and the last):
   * route: bit-exact for every query cluster on the GPU ratios;
   * attend: 16 queries (first 8 and last 8 rows) of each of three query
     clusters, against the oracle's materialised softmax rows;
-  * unpermute: bit-exact for the whole head.
+  * unpermute (run in the attention kernel's epilogue): the whole layer's
+    output bitwise equal to svgear_attend followed by svgear_unpermute.
 """
 import math
 
@@ -107,7 +108,8 @@ def test_full_layer_sampled_parity(layer, which):
     np.testing.assert_array_equal(f64(ra.sel_keys[h]), keys)
     assert np.all(keys <= wl.budget)
     # attend: sampled queries of three query clusters (ragged tails included)
-    op = f64(ra.op[h])
+    # the output is in the original query order: row pq[p] holds permuted query p
+    op = f64(ra.o[h])[pq]
     qp = f64(ra.qp[h])
     for c in rows[:3]:
         a, b = int(qo[c]), int(qo[c + 1])
@@ -118,5 +120,8 @@ def test_full_layer_sampled_parity(layer, which):
         err = np.linalg.norm(gotr - want) / np.linalg.norm(want)
         assert err <= 1e-2, (c, err)
         assert np.max(np.abs(gotr - want)) <= 2e-2, c
-    # unpermute
-    np.testing.assert_array_equal(f64(ra.o[h])[pq], op)
+    # unpermute in attend's epilogue == attend, then the standalone unpermute
+    from sparse_attention_video_means_amd import svgear as S
+    op_all = S.svgear_attend(ra.qp, ra.kp, ra.vp, ra.q_off, ra.k_off, ra.k_bar, ra.v_bar,
+                             ra.sel_mask, ra.scale)
+    assert torch.equal(S.svgear_unpermute(op_all, ra.perm_q), ra.o)

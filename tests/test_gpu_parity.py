@@ -304,3 +304,42 @@ def test_whole_path_is_deterministic():
     torch.cuda.synchronize()
     for key in ("labels_q", "labels_k", "perm_q", "ratio", "sel_mask", "op", "o"):
         assert torch.equal(outs[0][key], outs[1][key]), key
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_attend_unpermute_equals_attend_then_unpermute(name):
+    """The unpermutation run in attend's epilogue writes bitwise what attend
+    followed by the standalone unpermute writes (§3.1: outputs go back to the
+    original token order), for every case's routing."""
+    c = run_case(name)
+    wl, res = c["wl"], c["res"]
+    S = sv()
+    args = (res["qp"], res["kp"], res["vp"], res["q_off"], res["k_off"], res["k_bar"],
+            res["v_bar"], res["sel_mask"])
+    scale = 1 / math.sqrt(wl.d)
+    want = S.svgear_unpermute(S.svgear_attend(*args, scale), res["perm_q"])
+    got = S.svgear_attend_unpermute(*args, res["perm_q"], scale)
+    assert torch.equal(got, want)
+
+
+def test_attend_unpermute_drops_rows_outside_the_range():
+    """Permuted rows whose target lies outside [0, Nq) are not written; every
+    other row is."""
+    c = run_case("blobs_bf16_d64")
+    wl, res = c["wl"], c["res"]
+    S = sv()
+    args = (res["qp"], res["kp"], res["vp"], res["q_off"], res["k_off"], res["k_bar"],
+            res["v_bar"], res["sel_mask"])
+    scale = 1 / math.sqrt(wl.d)
+    want = S.svgear_unpermute(S.svgear_attend(*args, scale), res["perm_q"])
+    perm = res["perm_q"].clone()
+    lost = perm[:, :2].clone()
+    perm[:, 0] = -1
+    perm[:, 1] = wl.n
+    out = torch.full_like(want, 7.0)
+    S.svgear_attend_unpermute(*args, perm, scale, out=out)
+    for h in range(wl.heads):
+        kept = torch.ones(wl.n, dtype=torch.bool, device=out.device)
+        kept[lost[h].long()] = False
+        assert torch.equal(out[h][kept], want[h][kept])
+        assert bool((out[h][~kept] == 7.0).all())
