@@ -3,20 +3,19 @@
 //
 // Each block takes 256 rows of one head. Its four wavefronts keep their 64
 // rows as MFMA B operands in registers and stream the centroid table through
-// LDS in chunks of 64 centroids, fetching the next chunk into registers while
-// the current one is multiplied. The table already holds -2 * round(mu) in the
-// input element type and ||round(mu)||^2 in f32, so one chain of MFMAs seeded
-// with the norms yields ||mu||^2 - 2 x.mu directly. Each lane keeps a running
-// (distance, index) minimum over the centroids it sees in increasing index
-// order, two candidates at a time; four lanes share a row and are merged with
-// the lower index winning ties. The block then ranks its rows among equal labels (for the counting
-// sort that follows) without atomics.
+// LDS in chunks of 128 centroids (64 for f32), fetching the next chunk into
+// registers while the current one is multiplied. The table already holds
+// -2 * round(mu) in the input element type and ||round(mu)||^2 in f32, so one
+// chain of MFMAs seeded with the norms yields ||mu||^2 - 2 x.mu directly. Each
+// lane keeps a running (distance, index) minimum over the centroids it sees in
+// increasing index order, two candidates at a time; four lanes share a row and
+// are merged with the lower index winning ties. The block then ranks its rows
+// among equal labels (for the counting sort that follows) without atomics.
 #include "svgear_common.hpp"
 #include "svgear_internal.hpp"
 
 namespace svg {
 
-constexpr int kAssignChunk = 64;  // centroids staged per LDS pass
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X,
@@ -26,6 +25,8 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X,
                                                      int32_t* __restrict__ rank,
                                                      int32_t* __restrict__ hist) {
   constexpr int KC = D / 32;                       // 32-wide k chunks
+  // centroids staged per LDS pass (f32 rows are twice as wide: half as many)
+  constexpr int kAssignChunk = sizeof(T) == 2 ? 128 : 64;
   constexpr int LDR = D + 16 / sizeof(T);          // padded LDS row (elements)
   __shared__ __attribute__((aligned(16))) T tab[kAssignChunk * LDR];
   __shared__ float nrm[kAssignChunk];
