@@ -201,8 +201,8 @@ __global__ __launch_bounds__(256) void segsum_kernel(int N, int C, int nt, int m
     float acc[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
-    // eight rows in flight per thread; rows are still added in slot order
-    constexpr int U = 8;
+    // sixteen rows in flight per thread; rows are still added in slot order
+    constexpr int U = 16;
     for (int j = rg; j < len; j += U * RPI) {
       uint4 v[U];
 #pragma unroll
