@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void tile_prefix_kernel(int C, i
   const int t0 = min(tiles, w * per), t1 = min(tiles, t0 + per);
   int32_t* col = hist + size_t(h) * tiles * C + (ok ? c : 0);
   // reads go out kBatch at a time, so a run costs a few memory round trips
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 24;
   int sum = 0;
   if (ok)
     for (int tb = t0; tb < t1; tb += kBatch) {
