@@ -29,12 +29,13 @@ CFLAGS = [
 # Extra flags per source file. The attention kernel takes running maxima of
 # matrix-core results; with NaN inputs excluded the compiler drops the
 # quieting instructions IEEE mode would otherwise put before every v_max.
-# The assignment kernel compares every distance the matrix cores produce; with
-# the MFMA results in ordinary registers no accumulator-register read precedes
-# each comparison.
+# The assignment and probe kernels run vector arithmetic on every result the
+# matrix cores produce; with the MFMA results in ordinary registers no
+# accumulator-register read precedes it.
 FILE_FLAGS = {
     "svgear_attend.hip": ["-fno-honor-nans"],
     "svgear_kmeans.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "svgear_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
