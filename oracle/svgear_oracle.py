@@ -68,7 +68,7 @@ def round_operand(x, precision: str) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# cluster (Section 4.1: "We cluster Q and K using flash k-means")
+# cluster (Section 4.1: the rows of Q and of K are each grouped by k-means)
 # ----------------------------------------------------------------------------
 def kmeans_assign(x, mu, operand: str = "f64") -> np.ndarray:
     """Assignment step of Lloyd's k-means (Section 4.1).
@@ -272,10 +272,12 @@ def probe_values(q_centroids, kp, k_centroids, vp, v_centroids, k_offsets, scale
 # ----------------------------------------------------------------------------
 # route (Section 4.2 greedy selection; Section 5 per-query-cluster routing)
 # ----------------------------------------------------------------------------
-def route(ratio, k_offsets, budget_keys: int, fill: str = "skip"):
+def route(ratio, k_offsets, budget_keys: int, fill: str = "skip", q_offsets=None):
     """Greedy error-to-cost routing, one query cluster at a time.
 
-    For each query cluster: order the non-empty key clusters by ratio,
+    For each query cluster (with ``q_offsets`` given, each non-empty one: a
+    query cluster without queries has no attention row to route and selects
+    nothing): order the non-empty key clusters by ratio,
     highest first (equal ratios: lower key-cluster index first), and walk the
     order once; a key cluster is selected when its keys still fit the
     remaining budget of ``budget_keys`` exact keys (``fill="skip"``: a cluster
@@ -294,7 +296,10 @@ def route(ratio, k_offsets, budget_keys: int, fill: str = "skip"):
     cnt = np.zeros(cq, dtype=np.int32)
     used_keys = np.zeros(cq, dtype=np.int32)
     nonempty = np.nonzero(counts > 0)[0]
+    q_live = np.ones(cq, dtype=bool) if q_offsets is None else np.diff(np.asarray(q_offsets)) > 0
     for c in range(cq):
+        if not q_live[c]:
+            continue
         r = ratio[c, nonempty]
         order = nonempty[np.lexsort((nonempty, -r))]
         used = 0
@@ -315,9 +320,9 @@ def route_global(ratio, q_offsets, k_offsets, budget_entries: int, fill: str = "
     """Greedy error-to-cost routing over every block of a head at once.
 
     Section 4.1 bounds the number of exact entries of the block mask by
-    rho * N_q * N_k for the whole attention map, and Section 4.2 selects the
-    blocks with the highest error-to-size ratio first until that budget is
-    used. Here every block (c, c') with a non-empty query cluster c and a
+    rho * N_q * N_k for the whole attention map, and Section 4.2 takes
+    blocks in decreasing order of estimated error per entry until that
+    budget is spent. Here every block (c, c') with a non-empty query cluster c and a
     non-empty key cluster c' competes for one head-wide budget of
     ``budget_entries`` exact (query, key) entries, and a block costs
     |q_c| * |k_c'| entries (Section 5's split of the budget per query cluster
@@ -547,7 +552,7 @@ def routed_attention_head(q, k, v, cq: int, ck: int, budget_keys: int, iters: in
     if routing == "global":
         mask, lst, cnt, keys, _ = route_global(ratio, q_off, k_off, budget_keys)
     else:
-        mask, lst, cnt, keys = route(ratio, k_off, budget_keys)
+        mask, lst, cnt, keys = route(ratio, k_off, budget_keys, q_offsets=q_off)
     op = attend(qp, kp, vp, q_off, k_off, k_bar, v_bar, mask, scale)
     o = unpermute(op, perm_q)
     return RoutedResult(labels_q=labels_q, labels_k=labels_k, perm_q=perm_q, perm_k=perm_k,

@@ -78,3 +78,10 @@ def test_attend_worked_case():
     out = O.attend(np.asarray([g["query"]]), k, v, np.asarray([0, 1]), off, kc, vc,
                    np.zeros((1, 2), np.uint8), 1.0)
     np.testing.assert_allclose(out[0], g["output"], rtol=1e-13)
+
+
+def test_block_scores_worked_case():
+    g = load("block_scores_two_centroids.txt")
+    sc = O.block_scores(np.asarray(g["q_centroids"]), np.asarray(g["k_centroids"]),
+                        np.asarray(g["k_offsets"]), 1.0)
+    np.testing.assert_allclose(sc, np.asarray(g["scores"]), rtol=1e-13, atol=0)

@@ -213,6 +213,22 @@ def test_route_skip_and_continue_by_hand():
     assert keys[0] == 4
 
 
+def test_route_empty_query_cluster_selects_nothing():
+    # A query cluster without queries owns no attention row: with the query
+    # offsets given it selects nothing (empty mask row, list all -1, zero
+    # count and keys), whatever its ratios; the worked case above still holds
+    # for the live query cluster next to it.
+    counts = np.array([4, 6, 2, 3])
+    off = np.concatenate([[0], np.cumsum(counts)])
+    ratio = np.array([[0.9, 0.8, 0.1, 0.5], [0.9, 0.8, 0.1, 0.5]])
+    q_off = np.array([0, 0, 5])  # query cluster 0 empty, cluster 1 holds five queries
+    mask, lst, cnt, keys = O.route(ratio, off, 9, q_offsets=q_off)
+    np.testing.assert_array_equal(mask, [[0, 0, 0, 0], [1, 0, 1, 1]])
+    np.testing.assert_array_equal(lst, [[-1, -1, -1, -1], [0, 2, 3, -1]])
+    np.testing.assert_array_equal(cnt, [0, 3])
+    np.testing.assert_array_equal(keys, [0, 9])
+
+
 def test_route_ties_prefer_lower_index():
     counts = np.array([2, 2, 2, 2])
     off = np.concatenate([[0], np.cumsum(counts)])
