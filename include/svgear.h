@@ -39,7 +39,11 @@
  *    every buffer must stay valid until that work has completed.
  *  - Errors: argument problems are reported synchronously, before anything
  *    is enqueued (SVGEAR_ERR_INVALID_ARG, SVGEAR_ERR_UNSUPPORTED,
- *    SVGEAR_ERR_WORKSPACE). A failed kernel launch returns SVGEAR_ERR_HIP.
+ *    SVGEAR_ERR_WORKSPACE). Once the arguments pass, every call that launches
+ *    work checks that the calling thread's current HIP device is a gfx950
+ *    (looked up once per device, then cached) and returns
+ *    SVGEAR_ERR_UNSUPPORTED otherwise, also when no device is present. A
+ *    failed kernel launch returns SVGEAR_ERR_HIP.
  *    Faults inside kernels surface at the caller's next synchronisation, as
  *    for any asynchronous HIP work.
  *  - Calls hold no state between invocations and may be made from several
@@ -63,7 +67,8 @@ typedef struct ihipStream_t* svgear_stream_t; /* same object as hipStream_t */
 typedef enum {
   SVGEAR_OK = 0,
   SVGEAR_ERR_INVALID_ARG = 1, /* null pointer, size out of range, inconsistent sizes */
-  SVGEAR_ERR_UNSUPPORTED = 2, /* dtype or head dimension not built */
+  SVGEAR_ERR_UNSUPPORTED = 2, /* dtype or head dimension not built, or the current
+                                 device is not a gfx950 (MI355X) GPU */
   SVGEAR_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_workspace() */
   SVGEAR_ERR_HIP = 4          /* the HIP runtime refused a launch */
 } svgear_status;
@@ -203,23 +208,31 @@ svgear_status svgear_probe_values(svgear_dtype dt, int H, int Nk, int d, int Cq,
  * Greedy error-to-cost routing per query cluster (paper §4.2 "Error
  * estimation", §5 "Implementation": routing at query-cluster granularity).
  *
- * For every (head, query cluster): non-empty key clusters are ordered by
- * ratio, highest first, equal ratios by lower index; walking that order once,
- * a key cluster is selected when its keys still fit in `budget_keys` (clusters
- * that do not fit are passed over; later, smaller ones may still fit).
+ * For every (head, non-empty query cluster): non-empty key clusters are
+ * ordered by ratio, highest first, equal ratios by lower index; walking that
+ * order once, a key cluster is selected when its keys still fit in
+ * `budget_keys` (clusters that do not fit are passed over; later, smaller ones
+ * may still fit). A query cluster without queries selects nothing.
  * budget_keys = floor(rho * Nk) is computed by the caller.
  *
- *   ratio     [H][Cq][Ck] f32 in (>= 0 for non-empty clusters; the value of
- *             empty clusters is ignored).
+ *   ratio     [H][Cq][Ck] f32 in (>= 0 for non-empty clusters; NaN and negative
+ *             values count as 0; the value of empty clusters is ignored).
+ *   q_offsets [H][Cq+1] int32 in, or NULL (then every query cluster is routed).
  *   k_offsets [H][Ck+1] int32 in.
  *   sel_mask  [H][Cq][Ck] uint8 out (1 = exact).
  *   sel_list  [H][Cq][Ck] int32 out: selected key clusters ascending, -1 padded. May be NULL.
  *   sel_count [H][Cq] int32 out: number selected. May be NULL.
  *   sel_keys  [H][Cq] int32 out: exact keys used (<= budget_keys). May be NULL.
+ *   ws        svgear_route_workspace(H, Cq, Ck) bytes; that size is 0 (the sort
+ *             runs in on-chip memory), so ws may be NULL and ws_bytes 0.
+ * Returns SVGEAR_ERR_INVALID_ARG for sizes outside 1..1024, a negative budget or
+ * a NULL required pointer; nothing is launched then.
  */
-svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int32_t* k_offsets,
-                           int32_t budget_keys, uint8_t* sel_mask, int32_t* sel_list,
-                           int32_t* sel_count, int32_t* sel_keys, svgear_stream_t s);
+size_t svgear_route_workspace(int H, int Cq, int Ck);
+svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int32_t* q_offsets,
+                           const int32_t* k_offsets, int32_t budget_keys, uint8_t* sel_mask,
+                           int32_t* sel_list, int32_t* sel_count, int32_t* sel_keys, void* ws,
+                           size_t ws_bytes, svgear_stream_t s);
 
 /*
  * Greedy error-to-cost routing under one budget for the whole attention map of
@@ -274,6 +287,14 @@ svgear_status svgear_route_global(int H, int Cq, int Ck, const float* ratio,
  *       rows rounded to dt); may be NULL when that size is 0.
  * One head's K (and V) must span fewer than 2^32 bytes (Nk * d * element
  * bytes); larger heads return SVGEAR_ERR_INVALID_ARG.
+ * The selection enters as the mask alone: every block derives both its
+ * ascending list of selected key clusters and the list of skipped ones (which
+ * the compensation needs) from its mask row in one pass, so svgear_route's
+ * sel_list / sel_count are not taken here (a second description of the same
+ * selection could only disagree with the first).
+ * Inputs must be finite: the kernel is compiled on the assumption that no
+ * logit is NaN (running maxima skip NaN quieting); NaN inputs give undefined
+ * output values (never an out-of-bounds access).
  */
 size_t svgear_attend_workspace(svgear_dtype dt, int H, int Ck, int d);
 

@@ -77,7 +77,7 @@ def run(workload: str, densities, heads: int | None = None, n: int | None = None
         variants = (("topp_drop", scores, False), ("topp_comp", scores, True),
                     ("error_aware_comp", ratio_w, True), ("value_aware_comp", ratio_v, True))
         for name, ratio, comp in variants:
-            mask, _, _, keys = svgear.svgear_route(ratio, k_off, budget)
+            mask, _, _, keys = svgear.svgear_route(ratio, k_off, budget, q_off)
             err, zf, zs = svgear.svgear_map_error(qp, kp, q_off, k_off, res["k_bar"], mask,
                                                   scale, compensate=comp)
             rec = {"mse": float(err.double().sum()) / total,
@@ -116,7 +116,7 @@ def sweep_cq(workload: str, cqs, rho: float, heads: int | None = None, n: int | 
                 "delta_q2_mean": float(spread.mean()), "delta_q2_max": float(spread.max())}
         scores = svgear.svgear_block_scores(res["q_bar"], res["k_bar"], res["k_off"], scale)
         for name, ratio in (("error_aware_comp", res["ratio"]), ("topp_comp", scores)):
-            mask, _, _, _ = svgear.svgear_route(ratio, res["k_off"], budget)
+            mask, _, _, _ = svgear.svgear_route(ratio, res["k_off"], budget, res["q_off"])
             err, zf, zs = svgear.svgear_map_error(res["qp"], res["kp"], res["q_off"], res["k_off"],
                                                   res["k_bar"], mask, scale, compensate=True)
             line[name] = {"mse": float(err.double().sum()) / total,
@@ -154,7 +154,7 @@ def turbo(workload: str, settings, heads: int | None = None, n: int | None = Non
         for ev in events:
             for i, name in enumerate(ra.STAGES):
                 stages[name] += ev[2 * i].elapsed_time(ev[2 * i + 1]) / reps
-        core = sum(v for name, v in stages.items() if name != "unpermute")
+        core = sum(stages.values())
         qn = (ra.q_off[:, 1:] - ra.q_off[:, :-1]).double()
         line = {"workload": f"{wl.name}: H={wl.heads} N={wl.n} d={wl.d} {wl.dtype} "
                             f"iters={wl.iters}",
@@ -162,7 +162,7 @@ def turbo(workload: str, settings, heads: int | None = None, n: int | None = Non
                 "core_ms": core, "stages_ms": stages}
         scores = svgear.svgear_block_scores(ra.q_bar, ra.k_bar, ra.k_off, ra.scale)
         for name, mask in (("error_aware_comp", ra.sel_mask),
-                           ("topp_comp", svgear.svgear_route(scores, ra.k_off, wl.budget)[0])):
+                           ("topp_comp", svgear.svgear_route(scores, ra.k_off, wl.budget, ra.q_off)[0])):
             err, zf, zs = svgear.svgear_map_error(ra.qp, ra.kp, ra.q_off, ra.k_off, ra.k_bar, mask,
                                                   ra.scale, compensate=True)
             keys = mask.to(torch.int64).mul(

@@ -70,5 +70,44 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "libsvgear_san.so")
+# host-only sanitizers: each -fsanitize= applies to the host pass alone, device
+# code is built exactly as in the product library
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized() -> str:
+    """A build of the library whose ABI layer (argument validation, workspace
+    carving; csrc/svgear_api.hip) has its host code instrumented with
+    AddressSanitizer and UndefinedBehaviorSanitizer. The kernels and their
+    launchers are the product build's objects. Load it with the sanitizer
+    runtime preloaded (asan_runtime()) and SVGEAR_LIB pointing at it."""
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    objs = [os.path.join(BUILD, f[:-4] + ".o") for f in srcs if f != "svgear_api.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    api = os.path.join(BUILD, "svgear_api_san.o")
+    _run([HIPCC, *[f for f in CFLAGS if f != "-O3"], "-O1", "-g", *SAN_FLAGS, "-c",
+          os.path.join(CSRC, "svgear_api.hip"), "-o", api])
+    tmp = SAN_LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+          "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o",
+          tmp, api, *objs])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def asan_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the HIP toolchain."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm")
+    return hits[-1]
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized())

@@ -3,6 +3,9 @@
 // never allocates or synchronises, and returns the first launch error.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstring>
+
 #include "../../include/svgear.h"
 #include "svgear_internal.hpp"
 
@@ -10,14 +13,53 @@ using namespace svg;
 
 namespace {
 
-int elem_bytes(svgear_dtype dt) {
+// The kernels are built for gfx950 only. The architecture of the calling
+// thread's current device is looked up once per device and cached; a call on
+// any other device (or with no device at all) is refused before anything is
+// enqueued.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+svgear_status device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();  // leave no sticky error behind for the caller
+    return SVGEAR_ERR_UNSUPPORTED;
+  }
+  int state = dev < kMaxDevices ? g_arch_state[dev].load(std::memory_order_relaxed) : 0;
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    bool ok = hipGetDeviceProperties(&prop, dev) == hipSuccess;
+    if (!ok) (void)hipGetLastError();
+    // gcnArchName is "gfx950" optionally followed by ":feature+..." flags
+    ok = ok && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+         (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+    state = ok ? 1 : 2;
+    if (dev < kMaxDevices) g_arch_state[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? SVGEAR_OK : SVGEAR_ERR_UNSUPPORTED;
+}
+
+// A C caller may pass any int where the ABI names an enum, and C++ may not
+// read an enum object holding a value outside its enumerators. Entry points
+// therefore take the bytes of such a parameter as a plain int, without ever
+// reading it as the enum type.
+template <typename E>
+int enum_code(const E* e) {
+  static_assert(sizeof(E) == sizeof(int), "ABI enums are int-sized");
+  int v;
+  std::memcpy(&v, e, sizeof v);
+  return v;
+}
+
+int elem_bytes(int dt) {
   return dt == SVGEAR_BF16 ? 2 : (dt == SVGEAR_F32 ? 4 : 0);
 }
 
 bool dim_ok(int d) { return d == 64 || d == 128; }
 
 // Common shape check for a tensor family clustered into C clusters.
-svgear_status check_shape(svgear_dtype dt, int H, int N, int d, int C) {
+svgear_status check_shape(int dt, int H, int N, int d, int C) {
   if (H < 1 || N < 1 || C < 1 || C > N || C > kMaxClusters) return SVGEAR_ERR_INVALID_ARG;
   if (elem_bytes(dt) == 0 || !dim_ok(d)) return SVGEAR_ERR_UNSUPPORTED;
   if (size_t(H) * N * d > (size_t(1) << 40)) return SVGEAR_ERR_INVALID_ARG;
@@ -63,7 +105,14 @@ ClusterWs cluster_ws_carve(void* ws, int eb, int H, int N, int d, int C, int nt 
     if ((expr) != hipSuccess) return SVGEAR_ERR_HIP;       \
   } while (0)
 
-svgear_status attend_common(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
+// After the arguments are validated: refuse devices the kernels were not built for.
+#define SVG_NEED_DEVICE()                                  \
+  do {                                                     \
+    const svgear_status dev_st_ = device_ok();             \
+    if (dev_st_ != SVGEAR_OK) return dev_st_;              \
+  } while (0)
+
+svgear_status attend_common(int dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
                             float scale, const void* Qp, const void* Kp, const void* Vp,
                             const int32_t* q_offsets, const int32_t* k_offsets,
                             const float* k_centroids, const float* v_centroids,
@@ -80,6 +129,7 @@ svgear_status attend_common(svgear_dtype dt, int H, int Nq, int Nk, int d, int C
   if (size_t(Nk) * d * elem_bytes(dt) >= (size_t(1) << 32)) return SVGEAR_ERR_INVALID_ARG;
   const size_t need = attend_ws_bytes(elem_bytes(dt), H, Ck, d);
   if (need > 0 && (!ws || ws_bytes < need)) return SVGEAR_ERR_WORKSPACE;
+  SVG_NEED_DEVICE();
   SVG_TRY(launch_attend(elem_bytes(dt), H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets,
                         k_offsets, k_centroids, v_centroids, sel_mask, q_perm, Op, ws,
                         as_stream(s)));
@@ -90,30 +140,33 @@ svgear_status attend_common(svgear_dtype dt, int H, int Nq, int Nk, int d, int C
 
 extern "C" {
 
-const char* svgear_status_string(svgear_status st) {
-  switch (st) {
+const char* svgear_status_string(svgear_status st_in) {
+  switch (enum_code(&st_in)) {
     case SVGEAR_OK: return "ok";
     case SVGEAR_ERR_INVALID_ARG: return "invalid argument";
-    case SVGEAR_ERR_UNSUPPORTED: return "unsupported dtype or head dimension";
+    case SVGEAR_ERR_UNSUPPORTED: return "unsupported dtype, head dimension or device";
     case SVGEAR_ERR_WORKSPACE: return "workspace too small";
     case SVGEAR_ERR_HIP: return "HIP launch failure";
   }
   return "unknown status";
 }
 
-size_t svgear_cluster_workspace(svgear_dtype dt, int H, int N, int d, int C) {
+size_t svgear_cluster_workspace(svgear_dtype dt_in, int H, int N, int d, int C) {
+  const int dt = enum_code(&dt_in);
   if (check_shape(dt, H, N, d, C) != SVGEAR_OK) return 0;
   return cluster_ws_bytes(elem_bytes(dt), H, N, d, C);
 }
 
-svgear_status svgear_cluster(svgear_dtype dt, int H, int N, int d, int C, int iters,
+svgear_status svgear_cluster(svgear_dtype dt_in, int H, int N, int d, int C, int iters,
                              const void* X, float* centroids, int32_t* labels, int32_t* counts,
                              void* ws, size_t ws_bytes, svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   const svgear_status st = check_shape(dt, H, N, d, C);
   if (st != SVGEAR_OK) return st;
   if (iters < 1 || !X || !centroids || !labels || !counts) return SVGEAR_ERR_INVALID_ARG;
   const int eb = elem_bytes(dt);
   if (!ws || ws_bytes < cluster_ws_bytes(eb, H, N, d, C)) return SVGEAR_ERR_WORKSPACE;
+  SVG_NEED_DEVICE();
   const hipStream_t hs = as_stream(s);
   ClusterWs w = cluster_ws_carve(ws, eb, H, N, d, C);
   SVG_TRY(launch_table(eb, H, d, C, centroids, w.table, w.norms, hs));
@@ -133,16 +186,18 @@ svgear_status svgear_cluster(svgear_dtype dt, int H, int N, int d, int C, int it
   return SVGEAR_OK;
 }
 
-size_t svgear_cluster_permute_workspace(svgear_dtype dt, int H, int N, int d, int C) {
+size_t svgear_cluster_permute_workspace(svgear_dtype dt_in, int H, int N, int d, int C) {
+  const int dt = enum_code(&dt_in);
   if (check_shape(dt, H, N, d, C) != SVGEAR_OK) return 0;
   return cluster_ws_bytes(elem_bytes(dt), H, N, d, C, 2);
 }
 
-svgear_status svgear_cluster_permute(svgear_dtype dt, int H, int N, int d, int C, int iters,
+svgear_status svgear_cluster_permute(svgear_dtype dt_in, int H, int N, int d, int C, int iters,
                                      int ntensors, const void* const* src, void* const* dst,
                                      float* const* means, float* centroids, int32_t* labels,
                                      int32_t* counts, int32_t* perm, int32_t* offsets, void* ws,
                                      size_t ws_bytes, svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   const svgear_status st = check_shape(dt, H, N, d, C);
   if (st != SVGEAR_OK) return st;
   if (iters < 1 || ntensors < 1 || ntensors > 2 || !src || !dst || !centroids || !labels ||
@@ -152,6 +207,7 @@ svgear_status svgear_cluster_permute(svgear_dtype dt, int H, int N, int d, int C
     if (!src[k] || !dst[k] || src[k] == dst[k]) return SVGEAR_ERR_INVALID_ARG;
   const int eb = elem_bytes(dt);
   if (!ws || ws_bytes < cluster_ws_bytes(eb, H, N, d, C, 2)) return SVGEAR_ERR_WORKSPACE;
+  SVG_NEED_DEVICE();
   const hipStream_t hs = as_stream(s);
   ClusterWs w = cluster_ws_carve(ws, eb, H, N, d, C, 2);
   const void* X = src[0];
@@ -190,15 +246,17 @@ svgear_status svgear_cluster_permute(svgear_dtype dt, int H, int N, int d, int C
   return SVGEAR_OK;
 }
 
-size_t svgear_permute_workspace(svgear_dtype dt, int H, int N, int d, int C) {
+size_t svgear_permute_workspace(svgear_dtype dt_in, int H, int N, int d, int C) {
+  const int dt = enum_code(&dt_in);
   if (check_shape(dt, H, N, d, C) != SVGEAR_OK) return 0;
   return sort_ws_bytes(H, N, d, C, 2);
 }
 
-svgear_status svgear_permute(svgear_dtype dt, int H, int N, int d, int C, const int32_t* labels,
+svgear_status svgear_permute(svgear_dtype dt_in, int H, int N, int d, int C, const int32_t* labels,
                              int32_t* perm, int32_t* offsets, int ntensors,
                              const void* const* src, void* const* dst, float* const* means,
                              void* ws, size_t ws_bytes, svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   const svgear_status st = check_shape(dt, H, N, d, C);
   if (st != SVGEAR_OK) return st;
   if (!labels || !perm || !offsets || ntensors < 1 || ntensors > 2 || !src || !dst)
@@ -207,6 +265,7 @@ svgear_status svgear_permute(svgear_dtype dt, int H, int N, int d, int C, const 
     if (!src[k] || !dst[k] || src[k] == dst[k]) return SVGEAR_ERR_INVALID_ARG;
   if (!ws || ws_bytes < sort_ws_bytes(H, N, d, C, 2)) return SVGEAR_ERR_WORKSPACE;
   const int eb = elem_bytes(dt);
+  SVG_NEED_DEVICE();
   const hipStream_t hs = as_stream(s);
   SortWs w = sort_ws_carve(ws, H, N, d, C, 2);
   SVG_TRY(launch_label_rank(labels, H, N, C, w.rank, w.hist, hs));
@@ -235,46 +294,58 @@ size_t svgear_probe_values_workspace(int H, int Nk, int Cq, int Ck) {
   return probe_ws_bytes(H, Nk, Cq, Ck, true);
 }
 
-svgear_status svgear_probe_values(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck,
+svgear_status svgear_probe_values(svgear_dtype dt_in, int H, int Nk, int d, int Cq, int Ck,
                                   float scale, const float* q_centroids, const void* Kp,
                                   const float* k_centroids, const void* Vp,
                                   const float* v_centroids, const int32_t* k_offsets,
                                   float* ratio, float* log_norm, void* ws, size_t ws_bytes,
                                   svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   const svgear_status st = check_shape(dt, H, Nk, d, Ck);
   if (st != SVGEAR_OK) return st;
   if (Cq < 1 || Cq > kMaxClusters || !(scale > 0.f) || !q_centroids || !Kp || !k_centroids ||
       !Vp || !v_centroids || !k_offsets || !ratio)
     return SVGEAR_ERR_INVALID_ARG;
   if (!ws || ws_bytes < probe_ws_bytes(H, Nk, Cq, Ck, true)) return SVGEAR_ERR_WORKSPACE;
+  SVG_NEED_DEVICE();
   SVG_TRY(launch_probe(elem_bytes(dt), H, Nk, d, Cq, Ck, scale, q_centroids, Kp, k_centroids, Vp,
                        v_centroids, k_offsets, ws, ratio, log_norm, as_stream(s)));
   return SVGEAR_OK;
 }
 
-svgear_status svgear_probe(svgear_dtype dt, int H, int Nk, int d, int Cq, int Ck, float scale,
+svgear_status svgear_probe(svgear_dtype dt_in, int H, int Nk, int d, int Cq, int Ck, float scale,
                            const float* q_centroids, const void* Kp, const float* k_centroids,
                            const int32_t* k_offsets, float* ratio, float* log_norm, void* ws,
                            size_t ws_bytes, svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   const svgear_status st = check_shape(dt, H, Nk, d, Ck);
   if (st != SVGEAR_OK) return st;
   if (Cq < 1 || Cq > kMaxClusters || !(scale > 0.f) || !q_centroids || !Kp || !k_centroids ||
       !k_offsets || !ratio)
     return SVGEAR_ERR_INVALID_ARG;
   if (!ws || ws_bytes < probe_ws_bytes(H, Nk, Cq, Ck, false)) return SVGEAR_ERR_WORKSPACE;
+  SVG_NEED_DEVICE();
   SVG_TRY(launch_probe(elem_bytes(dt), H, Nk, d, Cq, Ck, scale, q_centroids, Kp, k_centroids,
                        nullptr, nullptr, k_offsets, ws, ratio, log_norm, as_stream(s)));
   return SVGEAR_OK;
 }
 
-svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int32_t* k_offsets,
-                           int32_t budget_keys, uint8_t* sel_mask, int32_t* sel_list,
-                           int32_t* sel_count, int32_t* sel_keys, svgear_stream_t s) {
+size_t svgear_route_workspace(int H, int Cq, int Ck) {
+  (void)H; (void)Cq; (void)Ck;
+  return 0;  // the per-query-cluster router keeps its sort in LDS
+}
+
+svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int32_t* q_offsets,
+                           const int32_t* k_offsets, int32_t budget_keys, uint8_t* sel_mask,
+                           int32_t* sel_list, int32_t* sel_count, int32_t* sel_keys, void* ws,
+                           size_t ws_bytes, svgear_stream_t s) {
   if (H < 1 || Cq < 1 || Ck < 1 || Cq > kMaxClusters || Ck > kMaxClusters || budget_keys < 0 ||
       !ratio || !k_offsets || !sel_mask)
     return SVGEAR_ERR_INVALID_ARG;
-  SVG_TRY(launch_route(H, Cq, Ck, ratio, k_offsets, budget_keys, sel_mask, sel_list, sel_count,
-                       sel_keys, as_stream(s)));
+  (void)ws; (void)ws_bytes;  // svgear_route_workspace() is 0: nothing to check
+  SVG_NEED_DEVICE();
+  SVG_TRY(launch_route(H, Cq, Ck, ratio, q_offsets, k_offsets, budget_keys, sel_mask, sel_list,
+                       sel_count, sel_keys, as_stream(s)));
   return SVGEAR_OK;
 }
 
@@ -292,43 +363,49 @@ svgear_status svgear_route_global(int H, int Cq, int Ck, const float* ratio,
       budget_entries < 0 || !ratio || !q_offsets || !k_offsets || !sel_mask)
     return SVGEAR_ERR_INVALID_ARG;
   if (!ws || ws_bytes < route_global_ws_bytes(H, Cq, Ck)) return SVGEAR_ERR_WORKSPACE;
+  SVG_NEED_DEVICE();
   SVG_TRY(launch_route_global(H, Cq, Ck, ratio, q_offsets, k_offsets, budget_entries, sel_mask,
                               sel_list, sel_count, sel_keys, used_entries, ws, as_stream(s)));
   return SVGEAR_OK;
 }
 
-size_t svgear_attend_workspace(svgear_dtype dt, int H, int Ck, int d) {
+size_t svgear_attend_workspace(svgear_dtype dt_in, int H, int Ck, int d) {
+  const int dt = enum_code(&dt_in);
   if (H < 1 || Ck < 1 || Ck > kMaxClusters || elem_bytes(dt) == 0 || !dim_ok(d)) return 0;
   return attend_ws_bytes(elem_bytes(dt), H, Ck, d);
 }
 
-svgear_status svgear_attend(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
+svgear_status svgear_attend(svgear_dtype dt_in, int H, int Nq, int Nk, int d, int Cq, int Ck,
                             float scale, const void* Qp, const void* Kp, const void* Vp,
                             const int32_t* q_offsets, const int32_t* k_offsets,
                             const float* k_centroids, const float* v_centroids,
                             const uint8_t* sel_mask, void* Op, void* ws, size_t ws_bytes,
                             svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   return attend_common(dt, H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets, k_offsets,
                        k_centroids, v_centroids, sel_mask, nullptr, Op, ws, ws_bytes, s);
 }
 
-svgear_status svgear_attend_unpermute(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq,
+svgear_status svgear_attend_unpermute(svgear_dtype dt_in, int H, int Nq, int Nk, int d, int Cq,
                                       int Ck, float scale, const void* Qp, const void* Kp,
                                       const void* Vp, const int32_t* q_offsets,
                                       const int32_t* k_offsets, const float* k_centroids,
                                       const float* v_centroids, const uint8_t* sel_mask,
                                       const int32_t* q_perm, void* O, void* ws, size_t ws_bytes,
                                       svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   if (!q_perm || O == Qp) return SVGEAR_ERR_INVALID_ARG;
   return attend_common(dt, H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets, k_offsets,
                        k_centroids, v_centroids, sel_mask, q_perm, O, ws, ws_bytes, s);
 }
 
-svgear_status svgear_unpermute(svgear_dtype dt, int H, int N, int d, const int32_t* perm,
+svgear_status svgear_unpermute(svgear_dtype dt_in, int H, int N, int d, const int32_t* perm,
                                const void* Xp, void* X, svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   const svgear_status st = check_shape(dt, H, N, d, 1);
   if (st != SVGEAR_OK) return st;
   if (!perm || !Xp || !X || Xp == X) return SVGEAR_ERR_INVALID_ARG;
+  SVG_NEED_DEVICE();
   SVG_TRY(launch_unpermute(elem_bytes(dt), H, N, d, perm, Xp, X, as_stream(s)));
   return SVGEAR_OK;
 }
@@ -339,6 +416,7 @@ svgear_status svgear_block_scores(int H, int d, int Cq, int Ck, float scale,
   if (H < 1 || Cq < 1 || Ck < 1 || Cq > kMaxClusters || Ck > kMaxClusters || !dim_ok(d) ||
       !(scale > 0.f) || !q_centroids || !k_centroids || !k_offsets || !scores)
     return SVGEAR_ERR_INVALID_ARG;
+  SVG_NEED_DEVICE();
   SVG_TRY(launch_block_scores(H, d, Cq, Ck, scale, q_centroids, k_centroids, k_offsets, scores,
                               as_stream(s)));
   return SVGEAR_OK;
@@ -349,12 +427,13 @@ size_t svgear_map_error_workspace(int H, int Nq, int Ck) {
   return map_error_ws_bytes(H, Nq, Ck);
 }
 
-svgear_status svgear_map_error(svgear_dtype dt, int H, int Nq, int Nk, int d, int Cq, int Ck,
+svgear_status svgear_map_error(svgear_dtype dt_in, int H, int Nq, int Nk, int d, int Cq, int Ck,
                                float scale, const void* Qp, const void* Kp,
                                const int32_t* q_offsets, const int32_t* k_offsets,
                                const float* k_centroids, const uint8_t* sel_mask, int compensate,
                                float* err, float* z_full, float* z_sparse, void* ws,
                                size_t ws_bytes, svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   svgear_status st = check_shape(dt, H, Nq, d, Cq);
   if (st != SVGEAR_OK) return st;
   st = check_shape(dt, H, Nk, d, Ck);
@@ -363,18 +442,21 @@ svgear_status svgear_map_error(svgear_dtype dt, int H, int Nq, int Nk, int d, in
       !err || !z_full || !z_sparse)
     return SVGEAR_ERR_INVALID_ARG;
   if (!ws || ws_bytes < map_error_ws_bytes(H, Nq, Ck)) return SVGEAR_ERR_WORKSPACE;
+  SVG_NEED_DEVICE();
   SVG_TRY(launch_map_error(elem_bytes(dt), H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, q_offsets,
                            k_offsets, k_centroids, sel_mask, compensate ? 1 : 0, err, z_full,
                            z_sparse, ws, as_stream(s)));
   return SVGEAR_OK;
 }
 
-svgear_status svgear_row_spread(svgear_dtype dt, int H, int N, int d, int C, const void* Xp,
+svgear_status svgear_row_spread(svgear_dtype dt_in, int H, int N, int d, int C, const void* Xp,
                                 const float* means, const int32_t* offsets, float* spread,
                                 svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
   const svgear_status st = check_shape(dt, H, N, d, C);
   if (st != SVGEAR_OK) return st;
   if (!Xp || !means || !offsets || !spread) return SVGEAR_ERR_INVALID_ARG;
+  SVG_NEED_DEVICE();
   SVG_TRY(launch_row_spread(elem_bytes(dt), H, N, d, C, Xp, means, offsets, spread,
                             as_stream(s)));
   return SVGEAR_OK;

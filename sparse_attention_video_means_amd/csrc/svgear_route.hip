@@ -16,8 +16,9 @@
 namespace svg {
 
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ ratio,
+                                                    const int32_t* __restrict__ qoff,
                                                     const int32_t* __restrict__ koff, int Cq,
-                                                    int Ck, int P, int budget,
+                                                    int Ck, int P, int budget_keys,
                                                     uint8_t* __restrict__ mask,
                                                     int32_t* __restrict__ list,
                                                     int32_t* __restrict__ count,
@@ -30,6 +31,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ ra
   const int h = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const int32_t* ko = koff + size_t(h) * (Ck + 1);
   const float* rr = ratio + (size_t(h) * Cq + c) * Ck;
+  // a query cluster without queries has no row to route: it selects nothing
+  const int32_t* qo = qoff ? qoff + size_t(h) * (Cq + 1) : nullptr;
+  const int budget = (qo && qo[c + 1] - qo[c] <= 0) ? 0 : budget_keys;
   for (int i = tid; i < P; i += 256) {
     uint64_t k = ~0ull;
     if (i < Ck) {
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ ra
     key[i] = k;
   }
   __syncthreads();
-  for (int k = 2; k <= P; k <<= 1) {
+  for (int k = 2; k <= (budget > 0 ? P : 1); k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < P; i += 256) {
         const int ixj = i ^ j;
@@ -354,13 +358,13 @@ hipError_t launch_route_global(int H, int Cq, int Ck, const float* ratio, const 
   return hipGetLastError();
 }
 
-hipError_t launch_route(int H, int Cq, int Ck, const float* ratio, const int32_t* koff,
-                        int32_t budget, uint8_t* mask, int32_t* list, int32_t* count,
-                        int32_t* keys, hipStream_t s) {
+hipError_t launch_route(int H, int Cq, int Ck, const float* ratio, const int32_t* qoff,
+                        const int32_t* koff, int32_t budget, uint8_t* mask, int32_t* list,
+                        int32_t* count, int32_t* keys, hipStream_t s) {
   int P = 1;
   while (P < Ck) P <<= 1;
-  hipLaunchKernelGGL(route_kernel, dim3(Cq, H), dim3(256), 0, s, ratio, koff, Cq, Ck, P, budget,
-                     mask, list, count, keys);
+  hipLaunchKernelGGL(route_kernel, dim3(Cq, H), dim3(256), 0, s, ratio, qoff, koff, Cq, Ck, P,
+                     budget, mask, list, count, keys);
   return hipGetLastError();
 }
 

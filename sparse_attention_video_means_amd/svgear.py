@@ -16,10 +16,12 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsvgear.so")
+# SVGEAR_LIB names another build of the same library (the host-sanitizer build
+# that the ABI tests load); by default the in-tree libsvgear.so.
+LIB_PATH = os.environ.get("SVGEAR_LIB") or os.path.join(_HERE, "libsvgear.so")
 
 F32, BF16 = 0, 1
-STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype or head dimension",
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype, head dimension or device",
           3: "workspace too small", 4: "HIP launch failure"}
 
 _lib = None
@@ -57,7 +59,9 @@ def lib() -> ctypes.CDLL:
             "svgear_probe_values_workspace": (sz, [i32, i32, i32, i32]),
             "svgear_probe_values": (i32, [i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
                                           vp, vp, vp, vp, sz, vp]),
-            "svgear_route": (i32, [i32, i32, i32, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]),
+            "svgear_route_workspace": (sz, [i32, i32, i32]),
+            "svgear_route": (i32, [i32, i32, i32, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp,
+                                   sz, vp]),
             "svgear_route_global_workspace": (sz, [i32, i32, i32]),
             "svgear_route_global": (i32, [i32, i32, i32, vp, vp, vp, ctypes.c_int64, vp, vp, vp,
                                           vp, vp, vp, sz, vp]),
@@ -85,7 +89,8 @@ EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
            "svgear_permute_workspace", "svgear_permute", "svgear_cluster_permute_workspace",
            "svgear_cluster_permute", "svgear_probe_workspace", "svgear_probe",
            "svgear_probe_values_workspace", "svgear_probe_values",
-           "svgear_route", "svgear_route_global_workspace", "svgear_route_global",
+           "svgear_route_workspace", "svgear_route", "svgear_route_global_workspace",
+           "svgear_route_global",
            "svgear_attend_workspace", "svgear_attend", "svgear_attend_unpermute",
            "svgear_unpermute",
            "svgear_block_scores", "svgear_map_error_workspace", "svgear_map_error",
@@ -113,15 +118,23 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None, device=None):
+    """Checks a tensor argument before its pointer goes to the library: dtype,
+    shape, a dense row-major layout, and the device (``device`` given: that
+    device; otherwise any GPU)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None:
+        if t.device != torch.device(device):
+            raise ValueError(f"{name} must be on {device}, got {t.device}")
+    elif not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
 
 
 def _ws(nbytes: int, device) -> torch.Tensor:
@@ -255,19 +268,27 @@ def svgear_probe_values(q_centroids, kp, k_centroids, vp, v_centroids, k_offsets
     return ratio, log_norm
 
 
-def svgear_route(ratio, k_offsets, budget_keys: int):
-    """Greedy selection. Returns (mask u8 [H,Cq,Ck], list i32 [H,Cq,Ck], count [H,Cq], keys [H,Cq])."""
+def svgear_route(ratio, k_offsets, budget_keys: int, q_offsets=None):
+    """Greedy selection per query cluster; with ``q_offsets`` ([H, Cq+1] int32)
+    an empty query cluster selects nothing. Returns (mask u8 [H,Cq,Ck],
+    list i32 [H,Cq,Ck], count [H,Cq], keys [H,Cq])."""
     _need(ratio, "ratio", torch.float32)
     H, Cq, Ck = ratio.shape
     _need(k_offsets, "k_offsets", torch.int32, (H, Ck + 1))
+    if q_offsets is not None:
+        _need(q_offsets, "q_offsets", torch.int32, (H, Cq + 1))
     dev = ratio.device
     mask = torch.empty((H, Cq, Ck), dtype=torch.uint8, device=dev)
     lst = torch.empty((H, Cq, Ck), dtype=torch.int32, device=dev)
     cnt = torch.empty((H, Cq), dtype=torch.int32, device=dev)
     keys = torch.empty((H, Cq), dtype=torch.int32, device=dev)
-    _check("svgear_route", lib().svgear_route(H, Cq, Ck, _ptr(ratio), _ptr(k_offsets),
-                                              int(budget_keys), _ptr(mask), _ptr(lst), _ptr(cnt),
-                                              _ptr(keys), _stream()))
+    L = lib()
+    nbytes = L.svgear_route_workspace(H, Cq, Ck)
+    ws = _ws(nbytes, dev) if nbytes > 0 else None
+    _check("svgear_route", L.svgear_route(H, Cq, Ck, _ptr(ratio), _ptr(q_offsets),
+                                          _ptr(k_offsets), int(budget_keys), _ptr(mask),
+                                          _ptr(lst), _ptr(cnt), _ptr(keys), _ptr(ws),
+                                          0 if ws is None else ws.numel(), _stream()))
     return mask, lst, cnt, keys
 
 
@@ -414,7 +435,19 @@ class RoutedAttention:
         self.ws = _ws(wsz, device)
         self._events = None
 
+    def check_inputs(self, q, k, v, init_q, init_k):
+        """Raises unless the inputs match the sizes, dtype and device this
+        object was built for (the kernels read exactly those extents)."""
+        H, nq, nk, d, cq, ck = self.H, self.nq, self.nk, self.d, self.cq, self.ck
+        dev = self.o.device
+        _need(q, "q", self.o.dtype, (H, nq, d), dev)
+        _need(k, "k", self.o.dtype, (H, nk, d), dev)
+        _need(v, "v", self.o.dtype, (H, nk, d), dev)
+        _need(init_q, "init_q", torch.float32, (H, cq, d), dev)
+        _need(init_k, "init_k", torch.float32, (H, ck, d), dev)
+
     def __call__(self, q, k, v, init_q, init_k, stage_events: bool = False):
+        self.check_inputs(q, k, v, init_q, init_k)
         L, s, dt = lib(), _stream(), self.dt
         H, nq, nk, d, cq, ck = self.H, self.nq, self.nk, self.d, self.cq, self.ck
         ws, wn = _ptr(self.ws), self.ws.numel()
@@ -450,10 +483,11 @@ class RoutedAttention:
                 _ptr(self.ratio), _ptr(self.log_norm), ws, wn, s))
         mark(5); mark(6)
         if self.routing == "cluster":
-            _check("svgear_route", L.svgear_route(H, cq, ck, _ptr(self.ratio), _ptr(self.k_off),
-                                                  self.budget, _ptr(self.sel_mask),
-                                                  _ptr(self.sel_list), _ptr(self.sel_count),
-                                                  _ptr(self.sel_keys), s))
+            _check("svgear_route", L.svgear_route(H, cq, ck, _ptr(self.ratio), _ptr(self.q_off),
+                                                  _ptr(self.k_off), self.budget,
+                                                  _ptr(self.sel_mask), _ptr(self.sel_list),
+                                                  _ptr(self.sel_count), _ptr(self.sel_keys), ws,
+                                                  wn, s))
         else:
             _check("svgear_route_global", L.svgear_route_global(
                 H, cq, ck, _ptr(self.ratio), _ptr(self.q_off), _ptr(self.k_off), self.budget,
@@ -565,7 +599,7 @@ def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q,
     else:
         ratio, log_norm = svgear_probe_values(q_bar, kp, k_bar, vp, v_bar, k_off, scale)
     if routing == "cluster":
-        mask, lst, cnt, keys = svgear_route(ratio, k_off, budget)
+        mask, lst, cnt, keys = svgear_route(ratio, k_off, budget, q_off)
     else:
         mask, lst, cnt, keys, res["used_entries"] = svgear_route_global(ratio, q_off, k_off,
                                                                         budget)

@@ -83,8 +83,13 @@ def test_argument_errors_return_before_any_launch(L):
     assert L.svgear_probe(1, 1, 100, 64, 4, 4, 0.0, fake, fake, fake, fake, fake, null, fake,
                           1 << 30, null) == 1
     # route: negative budget, Ck too large
-    assert L.svgear_route(1, 4, 4, fake, fake, -1, fake, null, null, null, null) == 1
-    assert L.svgear_route(1, 4, 2000, fake, fake, 5, fake, null, null, null, null) == 1
+    assert L.svgear_route(1, 4, 4, fake, fake, fake, -1, fake, null, null, null, null, 0,
+                          null) == 1
+    assert L.svgear_route(1, 4, 2000, fake, null, fake, 5, fake, null, null, null, null, 0,
+                          null) == 1
+    assert L.svgear_route(1, 4, 4, fake, fake, null, 5, fake, null, null, null, null, 0,
+                          null) == 1
+    assert L.svgear_route_workspace(40, 100, 500) == 0
     # fused cluster + permute: three tensors, aliasing, short workspace
     two = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     assert L.svgear_cluster_permute(1, 1, 100, 64, 4, 2, 3, two, two, None, fake, fake, fake,
@@ -141,3 +146,56 @@ def test_argument_errors_return_before_any_launch(L):
                                      fake, fake, fake, fake, fake, other, null, 0, null) == 3
     # unpermute: aliasing
     assert L.svgear_unpermute(1, 1, 100, 64, fake, fake, fake, null) == 1
+
+
+def _gpu_present():
+    import torch
+    return torch.cuda.is_available()
+
+
+def test_valid_calls_without_a_gfx950_device_are_refused(L):
+    """With arguments that pass validation, a call on a machine without a
+    gfx950 device returns SVGEAR_ERR_UNSUPPORTED instead of launching."""
+    if _gpu_present():
+        pytest.skip("a GPU is present: these fake pointers must not reach a launch")
+    fake = ctypes.c_void_p(0x1000)
+    other = ctypes.c_void_p(0x2000)
+    null = None
+    assert L.svgear_route(1, 4, 4, fake, null, fake, 5, fake, null, null, null, null, 0,
+                          null) == 2
+    assert L.svgear_unpermute(1, 1, 100, 64, fake, fake, other, null) == 2
+    assert L.svgear_block_scores(1, 64, 4, 4, 0.1, fake, fake, fake, fake, null) == 2
+    assert L.svgear_status_string(2) == b"unsupported dtype, head dimension or device"
+
+
+def test_routed_attention_checks_its_inputs_before_any_launch():
+    """RoutedAttention passes raw pointers of q, k, v and the initial tables to
+    the library, so it must refuse any tensor whose dtype, shape, layout or
+    device differs from what it was built for (the kernels would otherwise read
+    past the buffers)."""
+    import torch
+
+    from sparse_attention_video_means_amd import svgear
+    H, N, d, cq, ck = 2, 64, 64, 4, 8
+    ra = svgear.RoutedAttention(H, N, d, cq, ck, budget=16, iters=2, dtype=torch.bfloat16,
+                                device="cpu")
+    good = dict(q=torch.zeros(H, N, d, dtype=torch.bfloat16),
+                k=torch.zeros(H, N, d, dtype=torch.bfloat16),
+                v=torch.zeros(H, N, d, dtype=torch.bfloat16),
+                init_q=torch.zeros(H, cq, d), init_k=torch.zeros(H, ck, d))
+    ra.check_inputs(**good)   # matches: no error
+    bad = {
+        "q": torch.zeros(H, N, d),                                    # f32 for a bf16 object
+        "k": torch.zeros(H, N - 1, d, dtype=torch.bfloat16),         # shorter N
+        "v": torch.zeros(H, d, N, dtype=torch.bfloat16).transpose(1, 2),  # transposed view
+        "init_q": torch.zeros(H, cq + 1, d),                          # wrong cluster count
+        "init_k": torch.zeros(H, ck, d, dtype=torch.float64),         # wrong table dtype
+    }
+    for name, t in bad.items():
+        args = dict(good, **{name: t})
+        with pytest.raises((TypeError, ValueError), match=name):
+            ra(**args)
+    if not _gpu_present():
+        return
+    with pytest.raises(ValueError, match="q"):
+        ra.check_inputs(**dict(good, q=good["q"].cuda()))   # another device
