@@ -81,7 +81,7 @@ def test_value_aware_probe_route_and_attend(name):
         assert ok.all(), f"{(~ok).sum()} of {ok.size} ratios off; worst " \
                          f"{np.max(np.abs(got - ratio) / (np.abs(ratio) + 1e-30))}"
         np.testing.assert_allclose(f64(res["log_norm"][h]), log_norm, rtol=0, atol=5e-3)
-        mask, lst, cnt, keys = O.route(got, ko, wl.budget)
+        mask, lst, cnt, keys = O.route(got, ko, wl.budget, q_offsets=qo)
         np.testing.assert_array_equal(f64(res["sel_mask"][h]), mask)
         np.testing.assert_array_equal(f64(res["sel_keys"][h]), keys)
         want = O.attend(f64(res["qp"][h]), kp, vp, qo, ko, kb, vb, mask, scale)
