@@ -326,6 +326,29 @@ svgear_status svgear_attend_unpermute(svgear_dtype dt, int H, int Nq, int Nk, in
                                       svgear_stream_t s);
 
 /*
+ * svgear_attend_unpermute without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * with a fixed memory plan, harnesses that forbid hipMalloc). Arguments,
+ * results and errors as svgear_attend_unpermute, bitwise the same output.
+ *
+ * Its scratch (the centroid rows rounded to dt, 2 * H * Ck * d elements of dt
+ * for bf16, none for f32) lives in a 32 MiB array of device memory that the
+ * library reserves on every GPU it runs on until the process ends; sizes that
+ * need more (bf16 with H * Ck * d above about 8.3 million) return
+ * SVGEAR_ERR_WORKSPACE before anything is enqueued. The call allocates and
+ * frees nothing. All calls on one GPU share that GPU's array: two calls that
+ * may overlap on one GPU (different streams, or host threads without
+ * ordering) race on it and must be ordered by the caller.
+ */
+svgear_status svgear_attend_unpermute_noalloc(svgear_dtype dt, int H, int Nq, int Nk, int d,
+                                              int Cq, int Ck, float scale, const void* Qp,
+                                              const void* Kp, const void* Vp,
+                                              const int32_t* q_offsets, const int32_t* k_offsets,
+                                              const float* k_centroids, const float* v_centroids,
+                                              const uint8_t* sel_mask, const int32_t* q_perm,
+                                              void* O, svgear_stream_t s);
+
+/*
  * Inverse permutation of output rows: X[h][perm[h][p]] = Xp[h][p] (paper §3.1).
  *   perm [H][N] int32 (a permutation of 0..N-1 per head); Xp, X [H][N][d] dt, not aliased.
  */

@@ -52,6 +52,34 @@ int enum_code(const E* e) {
   return v;
 }
 
+// Scratch memory of svgear_attend_unpermute_noalloc, for callers that cannot
+// allocate: one array per GPU, alive until the process ends. Host code never
+// uses the array's name as an address (on the host it only names the symbol);
+// the device address is looked up once per device with that device current
+// and kept in g_scratch.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array.
+svgear_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return SVGEAR_ERR_UNSUPPORTED;
+  }
+  void* p = dev < kMaxDevices ? g_scratch[dev].load(std::memory_order_acquire) : nullptr;
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return SVGEAR_ERR_HIP;
+    }
+    if (dev < kMaxDevices) g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SVGEAR_OK;
+}
+
 int elem_bytes(int dt) {
   return dt == SVGEAR_BF16 ? 2 : (dt == SVGEAR_F32 ? 4 : 0);
 }
@@ -397,6 +425,35 @@ svgear_status svgear_attend_unpermute(svgear_dtype dt_in, int H, int Nq, int Nk,
   if (!q_perm || O == Qp) return SVGEAR_ERR_INVALID_ARG;
   return attend_common(dt, H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets, k_offsets,
                        k_centroids, v_centroids, sel_mask, q_perm, O, ws, ws_bytes, s);
+}
+
+svgear_status svgear_attend_unpermute_noalloc(svgear_dtype dt_in, int H, int Nq, int Nk, int d,
+                                              int Cq, int Ck, float scale, const void* Qp,
+                                              const void* Kp, const void* Vp,
+                                              const int32_t* q_offsets, const int32_t* k_offsets,
+                                              const float* k_centroids, const float* v_centroids,
+                                              const uint8_t* sel_mask, const int32_t* q_perm,
+                                              void* O, svgear_stream_t s) {
+  const int dt = enum_code(&dt_in);
+  if (!q_perm || O == Qp) return SVGEAR_ERR_INVALID_ARG;
+  svgear_status st = check_shape(dt, H, Nq, d, Cq);
+  if (st != SVGEAR_OK) return st;
+  st = check_shape(dt, H, Nk, d, Ck);
+  if (st != SVGEAR_OK) return st;
+  if (!(scale > 0.f) || !Qp || !Kp || !Vp || !q_offsets || !k_offsets || !k_centroids ||
+      !v_centroids || !sel_mask || !O)
+    return SVGEAR_ERR_INVALID_ARG;
+  // the centroid rows rounded to dt must fit the scratch array
+  if (attend_ws_bytes(elem_bytes(dt), H, Ck, d) > kNoallocScratchBytes)
+    return SVGEAR_ERR_WORKSPACE;
+  // attend_common repeats the full argument check before its launch
+  SVG_NEED_DEVICE();
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != SVGEAR_OK) return st;
+  return attend_common(dt, H, Nq, Nk, d, Cq, Ck, scale, Qp, Kp, Vp, q_offsets, k_offsets,
+                       k_centroids, v_centroids, sel_mask, q_perm, O, ws, kNoallocScratchBytes,
+                       s);
 }
 
 svgear_status svgear_unpermute(svgear_dtype dt_in, int H, int N, int d, const int32_t* perm,

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
                                     vp, vp, vp, vp, sz, vp]),
             "svgear_attend_unpermute": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp,
                                               vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "svgear_attend_unpermute_noalloc": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp,
+                                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "svgear_unpermute": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
             "svgear_block_scores": (i32, [i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]),
             "svgear_map_error_workspace": (sz, [i32, i32, i32]),
@@ -92,7 +94,7 @@ EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
            "svgear_route_workspace", "svgear_route", "svgear_route_global_workspace",
            "svgear_route_global",
            "svgear_attend_workspace", "svgear_attend", "svgear_attend_unpermute",
-           "svgear_unpermute",
+           "svgear_attend_unpermute_noalloc", "svgear_unpermute",
            "svgear_block_scores", "svgear_map_error_workspace", "svgear_map_error",
            "svgear_row_spread")
 
@@ -368,6 +370,31 @@ def svgear_attend_unpermute(qp, kp, vp, q_offsets, k_offsets, k_centroids, v_cen
         _ptr(q_offsets), _ptr(k_offsets), _ptr(k_centroids), _ptr(v_centroids), _ptr(sel_mask),
         _ptr(q_perm), _ptr(o), _ptr(ws), ws.numel(), _stream()))
     return o
+
+
+def svgear_attend_unpermute_noalloc(qp, kp, vp, q_offsets, k_offsets, k_centroids, v_centroids,
+                                    sel_mask, q_perm, scale: float, out):
+    """svgear_attend_unpermute with the library's own scratch array instead of
+    a workspace: nothing is allocated (``out`` is required). Calls that may
+    overlap on one GPU race on that array."""
+    _need(qp, "qp")
+    H, Nq, d = qp.shape
+    Nk = kp.shape[1]
+    Cq, Ck = q_offsets.shape[1] - 1, k_offsets.shape[1] - 1
+    _need(kp, "kp", qp.dtype, (H, Nk, d))
+    _need(vp, "vp", qp.dtype, (H, Nk, d))
+    _need(q_offsets, "q_offsets", torch.int32, (H, Cq + 1))
+    _need(k_offsets, "k_offsets", torch.int32, (H, Ck + 1))
+    _need(k_centroids, "k_centroids", torch.float32, (H, Ck, d))
+    _need(v_centroids, "v_centroids", torch.float32, (H, Ck, d))
+    _need(sel_mask, "sel_mask", torch.uint8, (H, Cq, Ck))
+    _need(q_perm, "q_perm", torch.int32, (H, Nq))
+    _need(out, "out", qp.dtype, qp.shape)
+    _check("svgear_attend_unpermute_noalloc", lib().svgear_attend_unpermute_noalloc(
+        _dt(qp), H, Nq, Nk, d, Cq, Ck, float(scale), _ptr(qp), _ptr(kp), _ptr(vp),
+        _ptr(q_offsets), _ptr(k_offsets), _ptr(k_centroids), _ptr(v_centroids), _ptr(sel_mask),
+        _ptr(q_perm), _ptr(out), _stream()))
+    return out
 
 
 def svgear_unpermute(xp, perm, out=None):

@@ -146,6 +146,17 @@ def test_argument_errors_return_before_any_launch(L):
                                      fake, fake, fake, fake, fake, other, null, 0, null) == 3
     # unpermute: aliasing
     assert L.svgear_unpermute(1, 1, 100, 64, fake, fake, fake, null) == 1
+    # allocation-free attend: q_perm required, O must not alias Qp, and a
+    # problem whose rounded centroid rows exceed the fixed scratch is refused
+    assert L.svgear_attend_unpermute_noalloc(1, 1, 100, 100, 64, 4, 11, 0.1, fake, fake, fake,
+                                             fake, fake, fake, fake, fake, null, other,
+                                             null) == 1
+    assert L.svgear_attend_unpermute_noalloc(1, 1, 100, 100, 64, 4, 11, 0.1, fake, fake, fake,
+                                             fake, fake, fake, fake, fake, fake, fake,
+                                             null) == 1
+    assert L.svgear_attend_unpermute_noalloc(1, 80, 4096, 4096, 128, 8, 1024, 0.1, fake, fake,
+                                             fake, fake, fake, fake, fake, fake, fake, other,
+                                             null) == 3
 
 
 def _gpu_present():
