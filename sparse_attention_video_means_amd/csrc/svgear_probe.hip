@@ -47,7 +47,8 @@ __global__ __launch_bounds__(1024) void probe_units_kernel(int Ck, const int32_t
   if (tid == 0) unit_prefix[size_t(h) * (Ck + 1) + Ck] = total;
 }
 
-// st2[h][c][c'] = sl2 * qbar_c . kbar_c'  (16 x 16 pairs per block, rows from LDS)
+// st2[h][c'][c] = sl2 * qbar_c . kbar_c'  (16 x 16 pairs per block, rows from LDS;
+// query centroid fastest, so that one key cluster's logits are contiguous)
 template <int D>
 __global__ __launch_bounds__(256) void centroid_logits_kernel(int Cq, int Ck, float sl2,
                                                               const float* __restrict__ qc,
@@ -63,10 +64,13 @@ __global__ __launch_bounds__(256) void centroid_logits_kernel(int Cq, int Ck, fl
   }
   __syncthreads();
   const int a = tid / 16, b = tid % 16;
-  float dot = 0.f;
+  // in double: the probe subtracts this logit from each raw key's, so its
+  // rounding is the only error the pair shares (one f32 rounding at the end)
+  double dot = 0.0;
 #pragma unroll 8
-  for (int j = 0; j < D; ++j) dot = fmaf(qs[a][j], kcs[b][j], dot);
-  if (c0 + a < Cq && k0 + b < Ck) st2[(size_t(h) * Cq + c0 + a) * Ck + k0 + b] = dot * sl2;
+  for (int j = 0; j < D; ++j) dot = fma(double(qs[a][j]), double(kcs[b][j]), dot);
+  if (c0 + a < Cq && k0 + b < Ck)
+    st2[(size_t(h) * Ck + k0 + b) * Cq + c0 + a] = float(dot * double(sl2));
 }
 
 __device__ __forceinline__ int find_unit_cluster(const int32_t* prefix, int C, int q) {
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
   auto unit_start = [&](int cc) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      st[cb] = cok[cb] ? st2g[(size_t(h) * Cq + cidx[cb]) * Ck + cc] : 0.f;
+      st[cb] = cok[cb] ? st2g[(size_t(h) * Ck + cc) * Cq + cidx[cb]] : 0.f;
       mp[cb] = 0.f;  // reference relative to s~: m = s~ + mp, mp >= 0
       Z[cb] = 0.f;
       E[cb] = 0.f;
@@ -386,6 +390,314 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
   }
 }
 
+// ---- bf16 keys: raw key tiles copied straight into LDS ---------------------
+//
+// For bf16 keys the kernel below replaces the staging of (k - kbar): the
+// matrix cores take the raw keys (exact bf16) against q' = sl2 qbar carried
+// as three bf16 parts (q' = p0 + p1 + p2 to about 2^-27 relative, so the
+// products are exact and only the f32 accumulation rounds), and every
+// accumulator starts at -sl2 qbar.kbar (the centroid logit, formed in double
+// and rounded once). The result is the base-2 delta logit D_j = sl2 qbar.(k_j
+// - kbar) with no vector work per key: tiles of 64 keys are copied from HBM
+// into LDS by the buffer unit, already in MFMA fragment order (fragment
+// (rb, kc) = keys 16 rb .. +15, dims 32 kc .. +31: lane (r, g) holds key
+// 16 rb + r, dims 32 kc + 8 g .. +7), double-buffered so that the next tile
+// is in flight while the current one is multiplied.
+typedef __attribute__((address_space(3))) void probe_lds_void;
+
+// 16 (or 4) bytes at byte offset voff of [base, base + bytes) into LDS at
+// dst + size * lane (kept out of the kernel template's body, like the
+// attention kernel's copy helper).
+__device__ __forceinline__ void probe_copy_lds(const void* base, uint32_t bytes, uint32_t voff,
+                                               probe_lds_void* dst, int size) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+  if (size == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+}
+
+template <int D, bool VALUE>
+__global__ __launch_bounds__(256) void probe_bf16_kernel(
+    const float* __restrict__ qc, const __bf16* __restrict__ Kp, const int32_t* __restrict__ koff,
+    const int32_t* __restrict__ unit_prefix, const float* __restrict__ st2g,
+    const float2* __restrict__ vstat, int Nk, int Cq, int Ck, int maxu, float sl2,
+    float* __restrict__ rec) {
+  constexpr int RS = VALUE ? 4 : 3;
+  constexpr int KC = D / 32;
+  constexpr int FR = 4 * KC;   // 1 KB fragments per 64-key tile
+  constexpr int NI = FR / 4;   // copy instructions per wave and tile
+  constexpr int TILE = 64 * D;
+  // three tile buffers (copies run two tiles ahead), each a distinct LDS
+  // object so that the compiler tells the asynchronous fill of one from the
+  // reads of another
+  __shared__ __attribute__((aligned(16))) __bf16 kt0[TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 kt1[TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 kt2[TILE];
+  // (a_j, b_j) of the tile's keys, as two arrays of 64 floats
+  __shared__ __attribute__((aligned(16))) float va0[VALUE ? 64 : 4];
+  __shared__ __attribute__((aligned(16))) float vb0[VALUE ? 64 : 4];
+  __shared__ __attribute__((aligned(16))) float va1[VALUE ? 64 : 4];
+  __shared__ __attribute__((aligned(16))) float vb1[VALUE ? 64 : 4];
+  __shared__ __attribute__((aligned(16))) float va2[VALUE ? 64 : 4];
+  __shared__ __attribute__((aligned(16))) float vb2[VALUE ? 64 : 4];
+  // the centroid logits of the tile's key cluster: wave w's 64 floats hold its
+  // two centroid blocks at [64 w + 16 cb + r]
+  __shared__ __attribute__((aligned(16))) float sb0[256];
+  __shared__ __attribute__((aligned(16))) float sb1[256];
+  __shared__ __attribute__((aligned(16))) float sb2[256];
+  // copy instructions per wave and tile (the vmcnt of one tile's copies)
+  constexpr int CPT = NI + 1 + (VALUE ? 2 : 0);
+  static_assert(CPT < 16, "vmcnt field");
+
+  const int h = blockIdx.y, grp = blockIdx.z, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int32_t* up = unit_prefix + size_t(h) * (Ck + 1);
+  const int32_t* ko = koff + size_t(h) * (Ck + 1);
+  const int nunits = up[Ck];
+  if (int(blockIdx.x) >= nunits) return;  // uniform over the block
+
+  // B operands: centroid blocks w and w + 4 of the group's 8, q' in two parts
+  Frag<__bf16> bq[2][KC][2];
+  int cidx[2];
+  bool cok[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int c = grp * kProbeGroup + (w + 4 * cb) * 16 + r;
+    cidx[cb] = c;
+    cok[cb] = c < Cq;
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      // (a clamped row, loaded unconditionally: no branch per element)
+      const float4* qrow = reinterpret_cast<const float4*>(
+          qc + (size_t(h) * Cq + (cok[cb] ? c : 0)) * D + k * 32 + g * 8);
+      const float4 q0 = qrow[0], q1 = qrow[1];
+      const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = cok[cb] ? qv[e] * sl2 : 0.f;
+        const __bf16 p0 = __bf16(x);
+        bq[cb][k][0].v[e] = p0;
+        bq[cb][k][1].v[e] = __bf16(x - float(p0));  // the difference is exact
+      }
+    }
+  }
+  const bool blk_live[2] = {grp * kProbeGroup + w * 16 < Cq,
+                            grp * kProbeGroup + (w + 4) * 16 < Cq};
+
+  const uint32_t kbytes = uint32_t(size_t(Nk) * D * 2);
+  const __bf16* Kh = Kp + size_t(h) * Nk * D;
+  const float2* Vs = VALUE ? vstat + size_t(h) * Nk : nullptr;
+  const uint32_t vbytes = uint32_t(size_t(Nk) * 8);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+
+  struct Tile {
+    int u, cc, j0, j1, tj;
+  };
+  auto unit_tile = [&](int u) {
+    Tile t;
+    t.u = u;
+    t.cc = find_unit_cluster(up, Ck, u);
+    t.j0 = ko[t.cc] + (u - up[t.cc]) * kProbeUnit;
+    t.j1 = min(ko[t.cc + 1], t.j0 + kProbeUnit);
+    t.tj = t.j0;
+    return t;
+  };
+  // copies of one tile into (kt, va, vb); rows past the unit read its first
+  // row (finite data, masked out below)
+  const uint32_t sbytes = uint32_t(size_t(Ck) * Cq * 4);
+  const float* sth = st2g + size_t(h) * Ck * Cq;
+  // the centroid this lane copies the logit of (lanes 32..63 repeat 0..31)
+  const int scid = min(grp * kProbeGroup + (wu + 4 * ((lane >> 4) & 1)) * 16 + r, Cq - 1);
+  auto issue = [&](const Tile& t, __bf16* kt, float* va, float* vb, float* sb) {
+    probe_copy_lds(sth, sbytes, uint32_t(t.cc * Cq + scid) * 4, (probe_lds_void*)(sb + wu * 64), 4);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int f = wu * NI + i, rb = f / KC, kc = f % KC;
+      int row = t.tj + rb * 16 + r;
+      row = row < t.j1 ? row : t.j0;
+      probe_copy_lds(Kh, kbytes, uint32_t(row) * (D * 2) + (kc * 32 + g * 8) * 2,
+                     (probe_lds_void*)(kt + f * 512), 16);
+    }
+    if (VALUE && lane < 16) {  // wave w: keys 16 w .. 16 w + 15
+      const int k = t.tj + wu * 16 + lane;
+      const int key = k < t.j1 ? k : t.j0;
+      probe_copy_lds(Vs, vbytes, uint32_t(key) * 8, (probe_lds_void*)(va + wu * 16), 4);
+      probe_copy_lds(Vs, vbytes, uint32_t(key) * 8 + 4, (probe_lds_void*)(vb + wu * 16), 4);
+    }
+  };
+
+  float st[2], mp[2], Z[2], E[2], Ev[2], e2[2];
+  auto reset = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      mp[cb] = 0.f;  // reference relative to s~: m = s~ + mp, mp >= 0
+      Z[cb] = 0.f;
+      E[cb] = 0.f;
+      Ev[cb] = 0.f;
+      e2[cb] = 1.f;
+    }
+  };
+  // the next tile: the rest of this unit, else the first tile of the next
+  auto next_of = [&](const Tile& cur, bool& new_unit) {
+    Tile nxt = cur;
+    nxt.tj += 64;
+    new_unit = nxt.tj >= cur.j1;
+    if (new_unit) {
+      const int un = cur.u + int(gridDim.x);
+      if (un < nunits) nxt = unit_tile(un);
+      else nxt.u = nunits;  // none
+    }
+    return nxt;
+  };
+  // products and streaming sums of one tile held in (kt, va, vb). All four
+  // 16-key groups are multiplied first (eight independent accumulator chains
+  // per wave), then one rescale test per tile and the exponentials.
+  auto compute = [&](const Tile& cur, const __bf16* kt, const float* va, const float* vb,
+                     const float* sb) {
+    const int nvalid = min(64, cur.j1 - cur.tj);
+    st[0] = sb[wu * 64 + r];
+    st[1] = sb[wu * 64 + 16 + r];
+    const int ngrp = (nvalid + 15) >> 4;  // groups holding a key (uniform)
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb < ngrp) {
+        Frag<__bf16> a[KC];
+#pragma unroll
+        for (int k = 0; k < KC; ++k) a[k] = load8(kt + (kb * KC + k) * 512 + lane * 8);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          acc[cb][kb] = f32x4{-st[cb], -st[cb], -st[cb], -st[cb]};
+          if (!blk_live[cb]) continue;
+#pragma unroll
+          for (int k = 0; k < KC; ++k) {
+            mma(acc[cb][kb], a[k], bq[cb][k][0]);
+            mma(acc[cb][kb], a[k], bq[cb][k][1]);
+          }
+        }
+      }
+    }
+    // keys past the unit's end are masked out (uniform fast path for a full tile)
+    const bool full = nvalid == 64;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      if (!blk_live[cb]) continue;
+      float tmax = mp[cb];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb < ngrp) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (!full && kb * 16 + g * 4 + i >= nvalid) acc[cb][kb][i] = -__builtin_inff();
+            tmax = fmaxf(tmax, acc[cb][kb][i]);
+          }
+        }
+      }
+      if (tmax > mp[cb]) {
+        const float al = fast_exp2(mp[cb] - tmax);
+        Z[cb] *= al;
+        E[cb] *= al * al;
+        if (VALUE) Ev[cb] *= al * al;
+        mp[cb] = tmax;
+        e2[cb] = fast_exp2(-tmax);
+      }
+      const float m = mp[cb], ee = e2[cb];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (kb < ngrp) {
+          float ax[4], bx[4];
+          if (VALUE) {
+            const float4 xa = *reinterpret_cast<const float4*>(va + kb * 16 + g * 4);
+            const float4 xb = *reinterpret_cast<const float4*>(vb + kb * 16 + g * 4);
+            ax[0] = xa.x; ax[1] = xa.y; ax[2] = xa.z; ax[3] = xa.w;
+            bx[0] = xb.x; bx[1] = xb.y; bx[2] = xb.z; bx[3] = xb.w;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // a masked key gives e = 0 and dd = -ee: drop its square
+            const float e = fast_exp2(acc[cb][kb][i] - m);
+            const bool ok = full || kb * 16 + g * 4 + i < nvalid;
+            Z[cb] += e;
+            const float dd = ok ? e - ee : 0.f;
+            E[cb] = fmaf(dd, dd, E[cb]);
+            if (VALUE) Ev[cb] = fmaf(e, fmaf(dd, bx[i], e * ax[i]), Ev[cb]);
+          }
+        }
+      }
+    }
+  };
+  // a unit is done: merge the four lanes of each centroid and record it
+  auto record = [&](const Tile& cur) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float om = __shfl_xor(mp[cb], o, 64);
+        const float oZ = __shfl_xor(Z[cb], o, 64);
+        const float oE = __shfl_xor(E[cb], o, 64);
+        const float oV = VALUE ? __shfl_xor(Ev[cb], o, 64) : 0.f;
+        const float M = fmaxf(mp[cb], om);
+        const float a1 = fast_exp2(mp[cb] - M), a2 = fast_exp2(om - M);
+        Z[cb] = Z[cb] * a1 + oZ * a2;
+        E[cb] = E[cb] * (a1 * a1) + oE * (a2 * a2);
+        if (VALUE) Ev[cb] = Ev[cb] * (a1 * a1) + oV * (a2 * a2);
+        mp[cb] = M;
+      }
+      if (g == 0 && cok[cb]) {
+        float* o = rec + ((size_t(h) * Cq + cidx[cb]) * maxu + cur.u) * RS;
+        o[0] = st[cb] + mp[cb];  // absolute base-2 reference of this unit
+        o[1] = Z[cb];
+        o[2] = E[cb];
+        if (VALUE) o[3] = Ev[cb];
+      }
+    }
+  };
+  // one step: wait for the current tile's copies (leaving the next tile's in
+  // flight), start the copies two tiles ahead, multiply the current tile.
+  // cur, n1, n2 are the current tile and the next two (u == nunits: none);
+  // past the last tile the copies repeat the current one, so that every step
+  // issues and waits for the same number of copies.
+  // Returns false after the last tile.
+  auto step = [&](Tile& cur, Tile& n1, Tile& n2, const __bf16* kt, const float* va,
+                  const float* vb, const float* sb, __bf16* ktn, float* van, float* vbn,
+                  float* sbn) -> bool {
+    // vmcnt(CPT), lgkmcnt(0): every copy but n1's has landed
+    __builtin_amdgcn_s_waitcnt((CPT & 15) | (7 << 4) | ((CPT >> 4) << 14));
+    // every wave's copies of this tile have landed, and every wave is done
+    // with the buffer the new copies fill (the barrier adds no wait of its own)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(n2.u < nunits ? n2 : cur, ktn, van, vbn, sbn);
+    compute(cur, kt, va, vb, sb);
+    if (n1.u >= nunits || n1.u != cur.u) {
+      record(cur);
+      reset();
+    }
+    cur = n1;
+    n1 = n2;
+    if (n2.u < nunits) {
+      bool nu;
+      n2 = next_of(n2, nu);
+    }
+    return cur.u < nunits;
+  };
+
+  Tile cur = unit_tile(blockIdx.x);
+  reset();
+  bool nu;
+  Tile n1 = next_of(cur, nu);
+  Tile n2 = n1;
+  if (n1.u < nunits) n2 = next_of(n1, nu);
+  issue(cur, kt0, va0, vb0, sb0);
+  issue(n1.u < nunits ? n1 : cur, kt1, va1, vb1, sb1);
+  while (step(cur, n1, n2, kt0, va0, vb0, sb0, kt2, va2, vb2, sb2) &&
+         step(cur, n1, n2, kt1, va1, vb1, sb1, kt0, va0, vb0, sb0) &&
+         step(cur, n1, n2, kt2, va2, vb2, sb2, kt1, va1, vb1, sb1)) {
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
 template <bool VALUE>
 __global__ __launch_bounds__(256) void probe_finalize_kernel(int Cq, int Ck, int maxu,
                                                              const int32_t* __restrict__ koff,
@@ -460,9 +772,14 @@ static hipError_t probe_t(int H, int Nk, int Cq, int Ck, float sl2, const float*
   const int groups = ceil_div(Cq, kProbeGroup);
   int per_head = ceil_div(2048, H * groups);
   per_head = per_head < 1 ? 1 : (per_head > maxu ? maxu : per_head);
-  hipLaunchKernelGGL((probe_kernel<T, D, VALUE>), dim3(per_head, H, groups), dim3(256), 0, s, qc,
-                     static_cast<const T*>(Kp), kc, koff, up, st2, vstat, Nk, Cq, Ck, maxu, sl2,
-                     rec);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((probe_bf16_kernel<D, VALUE>), dim3(per_head, H, groups), dim3(256), 0, s,
+                       qc, static_cast<const __bf16*>(Kp), koff, up, st2, vstat, Nk, Cq, Ck, maxu,
+                       sl2, rec);
+  else
+    hipLaunchKernelGGL((probe_kernel<T, D, VALUE>), dim3(per_head, H, groups), dim3(256), 0, s,
+                       qc, static_cast<const T*>(Kp), kc, koff, up, st2, vstat, Nk, Cq, Ck, maxu,
+                       sl2, rec);
   return hipGetLastError();
 }
 

@@ -1,25 +1,29 @@
 """Rounding-error bound of the GPU probe's block ratios (test helper).
 
-The probe kernel forms, for query centroid c and permuted key j of key
-cluster c', the base-2 logit as st + D_j with
-    st  = sl2 q-bar_c . k-bar_c'          (f32 dot product, once per block)
-    D_j = sl2 q-bar_c . (k_j - k-bar_c')  (matrix cores: q-bar and k_j - k-bar
-                                           each split into a bf16 high part and
-                                           a bf16 remainder, the low x low
-                                           product dropped, f32 accumulation)
-where sl2 = scale log2(e). Per lane it streams e_j = 2^(D_j - mp) and
-dd_j = e_j - 2^(-mp) against a running reference mp >= 0, E = sum dd_j^2 and
-Z = sum e_j, and a finalize pass rescales every unit by a = 2^(st + mp - m)
-and divides: ratio = sum_units E a^2 / (Z^2 |k_c'|).
+For query centroid c and permuted key j of key cluster c' the probe needs
+the base-2 delta logit D_j = sl2 q-bar_c . (k_j - k-bar_c') (sl2 = scale
+log2(e)) and the centroid logit st = sl2 q-bar_c . k-bar_c', formed in double
+and rounded once to f32. It forms D_j in one of two ways:
+  * bf16 keys: the matrix cores take the raw keys (exact) against
+    q' = sl2 q-bar carried as two bf16 parts (a high part and the rounded
+    remainder, together within 2^-18 of q'), the accumulator starting at -st;
+    2 d/32 MFMAs of 32 exact products each;
+  * f32 keys: k_j - k-bar in f32, against q-bar, f32 matrix cores, times sl2.
+Per lane it then streams e_j = 2^(D_j - mp) and dd_j = e_j - 2^(-mp) against a
+running reference mp >= 0, E = sum dd_j^2 and Z = sum e_j, and a finalize pass
+rescales every unit by a = 2^(st + mp - m) and divides:
+ratio = sum_units E a^2 / (Z^2 |k_c'|).
 
 Every step's f32 rounding is bounded below (first order, unit roundoff 2^-24,
 the hardware exp2 taken to 3 ulp), from the same inputs the kernel received:
-  * D_j: u S_j + 2^-24 |D_j| with S_j = sl2 sum_d |q-bar_d| |k_jd - k-bar_d|;
-    for bf16 rows u = 3 2^-18 + 3 d 2^-24: each split factor is exact to
-    2^-18 relative, the dropped low x low product is below 2^-18 of the term,
-    and 3 d products are accumulated in f32 (worst case, linear in the count);
-    for f32 rows u = 2 d 2^-24 (one f32 product chain);
-  * st: sl2 d 2^-24 sum_d |q-bar_d k-bar_d| + 2^-23 |st|;
+  * D_j, bf16 keys: each MFMA's result is taken to carry an error of at most
+    33 2^-24 (|accumulator in| + sum |its 32 products|), i.e. the 32 products
+    summed one by one in f32 (the worst case, whatever the hardware's internal
+    order), which sums to (2 d/32 33 + 2) 2^-24 (|st| + sum_d |q'_d k_jd|)
+    with the scale and seed roundings, plus 2^-18 sum_d |q'_d k_jd| for the
+    two-part split;
+  * D_j, f32 keys: 2 d 2^-24 sl2 sum_d |q-bar_d| |k_jd - k-bar_d|;
+  * st in the finalize: 2 2^-24 |st|;
   * exponentials: 3 ulp plus the rounding of their arguments;
   * E: per key 2 |dd| delta(dd) + delta(dd)^2, plus the accumulation chain;
   * Z: the weighted mean of the per-key relative errors (a sum of positive
@@ -37,13 +41,6 @@ LN2 = math.log(2.0)
 ULP = 2.0 ** -24
 
 
-def unit(precision, d):
-    """Relative bound of the delta logit's rounding, per unit of S_j."""
-    if precision == "bf16":
-        return 3 * 2.0 ** -18 + 3 * d * ULP
-    return 2 * d * ULP
-
-
 def ratio_error_bound(qbar, kp, kbar, koff, scale, precision, mean_tol=0.0):
     """Absolute bound [Cq, Ck] on |ratio_gpu - ratio_exact| (0 where |k_c'| <= 1
     or the cluster is empty: the kernel writes those exactly)."""
@@ -56,14 +53,18 @@ def ratio_error_bound(qbar, kp, kbar, koff, scale, precision, mean_tol=0.0):
     n = np.diff(koff)
     kappa = np.repeat(np.arange(ck), n)
     sl2 = scale / LN2
-    u = unit(precision, d)
     dl = kp - kbar[kappa]                                   # [Nk, d]
     aq, adl = np.abs(qbar), np.abs(dl)
     D = sl2 * (qbar @ dl.T)                                 # [Cq, Nk] base-2 deltas
-    S = sl2 * (aq @ adl.T)
-    eta = u * S + ULP * np.abs(D)
     st = sl2 * (qbar @ kbar.T)                              # [Cq, Ck]
-    dst = sl2 * d * ULP * (aq @ np.abs(kbar).T) + 2 * ULP * np.abs(st)
+    if precision == "bf16":
+        n_mfma = 2 * (d // 32)
+        sqk = sl2 * (aq @ np.abs(kp).T)
+        eta = (n_mfma * 33 + 2) * ULP * (np.abs(st)[:, kappa] + sqk) + 2.0 ** -18 * sqk
+    else:
+        eta = 2 * d * ULP * sl2 * (aq @ adl.T)
+    eta = eta + ULP * np.abs(D)
+    dst = 2 * ULP * np.abs(st)
     if mean_tol > 0:
         eta = eta + sl2 * mean_tol * ((1 + aq) @ adl.T + aq @ (1 + np.abs(kbar[kappa])).T)
         dst = dst + sl2 * mean_tol * ((1 + aq) @ np.abs(kbar).T + aq @ (1 + np.abs(kbar)).T)

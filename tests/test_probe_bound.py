@@ -1,11 +1,11 @@
 """The probe's rounding-error bound (tests/probe_bound.py) against an f32
 emulation of the kernel's arithmetic (CPU only).
 
-The emulation follows the kernel's steps in float32: k_j - k-bar in f32,
-both factors split into a bf16 high part and a bf16 remainder, three
-products accumulated in f32, base-2 exponentials against a running
-reference, the squared gaps and the normaliser summed in f32, a rescale to
-the row maximum and the final division. Its ratios must stay within the
+The emulation follows the bf16 kernel's steps in float32: q' = sl2 q-bar
+split into two bf16 parts, raw bf16 keys, the accumulator seeded with the
+centroid logit and the products added in f32, base-2 exponentials against a
+running reference, the squared gaps and the normaliser summed in f32, a
+rescale to the row maximum and the final division. Its ratios must stay within the
 bound of the float64 values, and the bound must stay useful (well below the
 ratios themselves) on the blob-structured keys the workloads use.
 """
@@ -26,20 +26,27 @@ def bf16(x):
 
 
 def emulate_probe_f32(qbar, kp, kbar, koff, scale):
+    """The bf16 kernel's arithmetic in float32: q' = sl2 q-bar split into two
+    bf16 parts, the accumulator seeded with -sl2 q-bar.k-bar (double, rounded
+    once), 32 products per step added in f32, then the streaming sums."""
     f = np.float32
-    qbar, kp, kbar = (np.asarray(a, f) for a in (qbar, kp, kbar))
-    sl2 = f(scale * 1.4426950408889634)
+    qbar, kp, kbar = (np.asarray(a, np.float64) for a in (qbar, kp, kbar))
+    sl2d = scale * 1.4426950408889634
+    sl2 = f(sl2d)
     ck = koff.size - 1
     n = np.diff(koff)
     kappa = np.repeat(np.arange(ck), n)
-    dl = (kp - kbar[kappa]).astype(f)
-    dh = bf16(dl)
-    dlo = bf16((dl - dh).astype(f))
-    qh = bf16(qbar)
-    ql = bf16((qbar - qh).astype(f))
-    acc = (qh @ dh.T).astype(f) + (ql @ dh.T).astype(f) + (qh @ dlo.T).astype(f)
-    D = (acc * sl2).astype(f)
-    st = ((qbar @ kbar.T).astype(f) * sl2).astype(f)
+    qs = (qbar.astype(f) * sl2).astype(f)
+    p0 = bf16(qs)
+    p1 = bf16((qs - p0).astype(f))
+    st = (qbar.astype(f).astype(np.float64) @ kbar.astype(f).astype(np.float64).T * sl2d).astype(f)
+    kf = kp.astype(f)
+    acc = -st[:, kappa]
+    d = kp.shape[1]
+    for k in range(0, d, 32):
+        for part in (p0, p1):
+            acc = (acc + (part[:, k:k + 32] @ kf[:, k:k + 32].T).astype(f)).astype(f)
+    D = acc
     cq = qbar.shape[0]
     recs = []  # per block: (reference, Z, E)
     for c2 in range(ck):
