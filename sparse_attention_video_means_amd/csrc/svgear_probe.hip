@@ -29,6 +29,8 @@
 // (a_j, b_j) per permuted key and w per key cluster; the probe then also
 // streams Ev = sum e (e a_j + dd b_j) (e = exp2(s - m), dd = e - exp2(s~ - m))
 // and the finalize pass forms (Ev + w E) / (Z^2 |k_c'|).
+#include <type_traits>
+
 #include "svgear_common.hpp"
 #include "svgear_internal.hpp"
 
@@ -54,23 +56,38 @@ __global__ __launch_bounds__(256) void centroid_logits_kernel(int Cq, int Ck, fl
                                                               const float* __restrict__ qc,
                                                               const float* __restrict__ kc,
                                                               float* __restrict__ st2) {
-  __shared__ float qs[16][D + 1];
-  __shared__ float kcs[16][D + 1];
+  __shared__ __attribute__((aligned(16))) float qs[16][D + 4];
+  __shared__ __attribute__((aligned(16))) float kcs[16][D + 4];
   const int h = blockIdx.z, c0 = blockIdx.y * 16, k0 = blockIdx.x * 16, tid = threadIdx.x;
-  for (int i = tid; i < 16 * D; i += 256) {
-    const int r = i / D, j = i % D;
-    qs[r][j] = (c0 + r < Cq) ? qc[(size_t(h) * Cq + c0 + r) * D + j] : 0.f;
-    kcs[r][j] = (k0 + r < Ck) ? kc[(size_t(h) * Ck + k0 + r) * D + j] : 0.f;
+  constexpr int V = D / 4;  // float4 pieces per row
+  for (int i = tid; i < 16 * V; i += 256) {
+    const int r = i / V, j = (i % V) * 4;
+    // clamped rows, loaded unconditionally; rows past the end become zero
+    float4 x = *reinterpret_cast<const float4*>(qc + (size_t(h) * Cq + min(c0 + r, Cq - 1)) * D + j);
+    float4 y = *reinterpret_cast<const float4*>(kc + (size_t(h) * Ck + min(k0 + r, Ck - 1)) * D + j);
+    if (c0 + r >= Cq) x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k0 + r >= Ck) y = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(&qs[r][j]) = x;
+    *reinterpret_cast<float4*>(&kcs[r][j]) = y;
   }
   __syncthreads();
   const int a = tid / 16, b = tid % 16;
   // in double: the probe subtracts this logit from each raw key's, so its
-  // rounding is the only error the pair shares (one f32 rounding at the end)
-  double dot = 0.0;
+  // rounding is the only error the pair shares (one f32 rounding at the end);
+  // four interleaved partial sums shorten the dependent chain
+  double dot[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 8
-  for (int j = 0; j < D; ++j) dot = fma(double(qs[a][j]), double(kcs[b][j]), dot);
+  for (int j = 0; j < D; j += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(&qs[a][j]);
+    const float4 y = *reinterpret_cast<const float4*>(&kcs[b][j]);
+    dot[0] = fma(double(x.x), double(y.x), dot[0]);
+    dot[1] = fma(double(x.y), double(y.y), dot[1]);
+    dot[2] = fma(double(x.z), double(y.z), dot[2]);
+    dot[3] = fma(double(x.w), double(y.w), dot[3]);
+  }
   if (c0 + a < Cq && k0 + b < Ck)
-    st2[(size_t(h) * Ck + k0 + b) * Cq + c0 + a] = float(dot * double(sl2));
+    st2[(size_t(h) * Ck + k0 + b) * Cq + c0 + a] =
+        float(((dot[0] + dot[1]) + (dot[2] + dot[3])) * double(sl2));
 }
 
 __device__ __forceinline__ int find_unit_cluster(const int32_t* prefix, int C, int q) {
@@ -481,9 +498,6 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
       }
     }
   }
-  const bool blk_live[2] = {grp * kProbeGroup + w * 16 < Cq,
-                            grp * kProbeGroup + (w + 4) * 16 < Cq};
-
   const uint32_t kbytes = uint32_t(size_t(Nk) * D * 2);
   const __bf16* Kh = Kp + size_t(h) * Nk * D;
   const float2* Vs = VALUE ? vstat + size_t(h) * Nk : nullptr;
@@ -549,46 +563,49 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
     }
     return nxt;
   };
-  // products and streaming sums of one tile held in (kt, va, vb). All four
-  // 16-key groups are multiplied first (eight independent accumulator chains
-  // per wave), then one rescale test per tile and the exponentials.
-  auto compute = [&](const Tile& cur, const __bf16* kt, const float* va, const float* vb,
-                     const float* sb) {
-    const int nvalid = min(64, cur.j1 - cur.tj);
+  // products and streaming sums of one tile held in (kt, va, vb, sb). All
+  // 16-key groups are multiplied first (the two centroid blocks' chains
+  // interleaved, eight independent chains per wave), then one rescale test
+  // per tile and the exponentials. A full tile (64 keys of the unit) takes a
+  // branch-free path; the unit's last, partial tile masks the keys past its
+  // end. Both centroid blocks are always multiplied: a block without live
+  // centroids has zero operands and is never recorded.
+  auto compute_impl = [&](auto full_tag, const Tile& cur, const __bf16* kt, const float* va,
+                          const float* vb, const float* sb) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int nvalid = FULL ? 64 : min(64, cur.j1 - cur.tj);
+    const int ngrp = FULL ? 4 : (nvalid + 15) >> 4;  // groups holding a key (uniform)
     st[0] = sb[wu * 64 + r];
     st[1] = sb[wu * 64 + 16 + r];
-    const int ngrp = (nvalid + 15) >> 4;  // groups holding a key (uniform)
+    const f32x4 seed[2] = {f32x4{-st[0], -st[0], -st[0], -st[0]},
+                           f32x4{-st[1], -st[1], -st[1], -st[1]}};
     f32x4 acc[2][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      if (kb < ngrp) {
+      if (FULL || kb < ngrp) {
         Frag<__bf16> a[KC];
 #pragma unroll
         for (int k = 0; k < KC; ++k) a[k] = load8(kt + (kb * KC + k) * 512 + lane * 8);
+        acc[0][kb] = seed[0];
+        acc[1][kb] = seed[1];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          acc[cb][kb] = f32x4{-st[cb], -st[cb], -st[cb], -st[cb]};
-          if (!blk_live[cb]) continue;
+        for (int k = 0; k < KC; ++k)
 #pragma unroll
-          for (int k = 0; k < KC; ++k) {
-            mma(acc[cb][kb], a[k], bq[cb][k][0]);
-            mma(acc[cb][kb], a[k], bq[cb][k][1]);
+          for (int p = 0; p < 2; ++p) {
+            mma(acc[0][kb], a[k], bq[0][k][p]);
+            mma(acc[1][kb], a[k], bq[1][k][p]);
           }
-        }
       }
     }
-    // keys past the unit's end are masked out (uniform fast path for a full tile)
-    const bool full = nvalid == 64;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      if (!blk_live[cb]) continue;
       float tmax = mp[cb];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        if (kb < ngrp) {
+        if (FULL || kb < ngrp) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            if (!full && kb * 16 + g * 4 + i >= nvalid) acc[cb][kb][i] = -__builtin_inff();
+            if (!FULL && kb * 16 + g * 4 + i >= nvalid) acc[cb][kb][i] = -__builtin_inff();
             tmax = fmaxf(tmax, acc[cb][kb][i]);
           }
         }
@@ -602,9 +619,10 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
         e2[cb] = fast_exp2(-tmax);
       }
       const float m = mp[cb], ee = e2[cb];
+      float zs[2] = {0.f, 0.f}, es[2] = {0.f, 0.f}, vs2[2] = {0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        if (kb < ngrp) {
+        if (FULL || kb < ngrp) {
           float ax[4], bx[4];
           if (VALUE) {
             const float4 xa = *reinterpret_cast<const float4*>(va + kb * 16 + g * 4);
@@ -614,17 +632,25 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            // a masked key gives e = 0 and dd = -ee: drop its square
+            // a masked key gives e = 0 and dd = -ee: its square is dropped
+            const int pp = i & 1;
             const float e = fast_exp2(acc[cb][kb][i] - m);
-            const bool ok = full || kb * 16 + g * 4 + i < nvalid;
-            Z[cb] += e;
-            const float dd = ok ? e - ee : 0.f;
-            E[cb] = fmaf(dd, dd, E[cb]);
-            if (VALUE) Ev[cb] = fmaf(e, fmaf(dd, bx[i], e * ax[i]), Ev[cb]);
+            zs[pp] += e;
+            const float dd = (FULL || kb * 16 + g * 4 + i < nvalid) ? e - ee : 0.f;
+            es[pp] = fmaf(dd, dd, es[pp]);
+            if (VALUE) vs2[pp] = fmaf(e, fmaf(dd, bx[i], e * ax[i]), vs2[pp]);
           }
         }
       }
+      Z[cb] += zs[0] + zs[1];
+      E[cb] += es[0] + es[1];
+      if (VALUE) Ev[cb] += vs2[0] + vs2[1];
     }
+  };
+  auto compute = [&](const Tile& cur, const __bf16* kt, const float* va, const float* vb,
+                     const float* sb) {
+    if (cur.j1 - cur.tj >= 64) compute_impl(std::true_type{}, cur, kt, va, vb, sb);
+    else compute_impl(std::false_type{}, cur, kt, va, vb, sb);
   };
   // a unit is done: merge the four lanes of each centroid and record it
   auto record = [&](const Tile& cur) {
