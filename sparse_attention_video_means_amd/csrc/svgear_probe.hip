@@ -411,15 +411,15 @@ __global__ __launch_bounds__(256) void probe_kernel(const float* __restrict__ qc
 //
 // For bf16 keys the kernel below replaces the staging of (k - kbar): the
 // matrix cores take the raw keys (exact bf16) against q' = sl2 qbar carried
-// as three bf16 parts (q' = p0 + p1 + p2 to about 2^-27 relative, so the
-// products are exact and only the f32 accumulation rounds), and every
+// as two bf16 parts (q' = p0 + p1 to about 2^-17 relative), and every
 // accumulator starts at -sl2 qbar.kbar (the centroid logit, formed in double
-// and rounded once). The result is the base-2 delta logit D_j = sl2 qbar.(k_j
-// - kbar) with no vector work per key: tiles of 64 keys are copied from HBM
-// into LDS by the buffer unit, already in MFMA fragment order (fragment
-// (rb, kc) = keys 16 rb .. +15, dims 32 kc .. +31: lane (r, g) holds key
-// 16 rb + r, dims 32 kc + 8 g .. +7), double-buffered so that the next tile
-// is in flight while the current one is multiplied.
+// and rounded once), so that the result is the base-2 delta logit D_j =
+// sl2 qbar.(k_j - kbar) with no vector work per key before the
+// exponentials. Tiles of 64 keys are copied from HBM into LDS by the buffer
+// unit, already in MFMA fragment order (fragment (rb, kc) = keys 16 rb .. +15,
+// dims 32 kc .. +31: lane (r, g) holds key 16 rb + r, dims 32 kc + 8 g .. +7),
+// through three buffers, so that the next two tiles are in flight while the
+// current one is multiplied.
 typedef __attribute__((address_space(3))) void probe_lds_void;
 
 // 16 (or 4) bytes at byte offset voff of [base, base + bytes) into LDS at
@@ -470,8 +470,7 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
   const int w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int32_t* up = unit_prefix + size_t(h) * (Ck + 1);
   const int32_t* ko = koff + size_t(h) * (Ck + 1);
-  const int nunits = up[Ck];
-  if (int(blockIdx.x) >= nunits) return;  // uniform over the block
+  if (up[Ck] == 0) return;  // no keys in this head (uniform over the block)
 
   // B operands: centroid blocks w and w + 4 of the group's 8, q' in two parts
   Frag<__bf16> bq[2][KC][2];
@@ -504,17 +503,39 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
   const uint32_t vbytes = uint32_t(size_t(Nk) * 8);
   const int wu = __builtin_amdgcn_readfirstlane(w);
 
+  // A tile: unit u (keys [j0, j1) of cluster cc, whose keys end at kend),
+  // keys tj .. tj + 63 of it. u == kNone: no tile.
   struct Tile {
-    int u, cc, j0, j1, tj;
+    int u, cc, j0, j1, tj, kend;
   };
-  auto unit_tile = [&](int u) {
-    Tile t;
-    t.u = u;
-    t.cc = find_unit_cluster(up, Ck, u);
-    t.j0 = ko[t.cc] + (u - up[t.cc]) * kProbeUnit;
-    t.j1 = min(ko[t.cc + 1], t.j0 + kProbeUnit);
-    t.tj = t.j0;
-    return t;
+  constexpr int kNone = 0x7fffffff;
+  // The block's share of the head: the units whose first key lies in
+  // [J0, J1), where the head's blocks split its keys evenly. That is a run of
+  // consecutive units, which the block walks in order, so that finding the
+  // next unit takes at most a read of the next cluster's end (no search).
+  const int J0 = int(int64_t(Nk) * blockIdx.x / gridDim.x);
+  const int J1 = int(int64_t(Nk) * (blockIdx.x + 1) / gridDim.x);
+  // the unit after t (skipping empty clusters), or none
+  auto next_unit = [&](const Tile& t) {
+    Tile n = t;
+    n.u = t.u + 1;
+    if (t.j1 < t.kend) {
+      n.j0 = t.j1;
+    } else {
+      int c = t.cc + 1;
+      while (c < Ck && ko[c + 1] == t.kend) ++c;
+      if (c >= Ck) {
+        n.u = kNone;
+        return n;
+      }
+      n.cc = c;
+      n.j0 = t.kend;
+      n.kend = ko[c + 1];
+    }
+    if (n.j0 >= J1) n.u = kNone;
+    n.j1 = min(n.j0 + kProbeUnit, n.kend);
+    n.tj = n.j0;
+    return n;
   };
   // copies of one tile into (kt, va, vb); rows past the unit read its first
   // row (finite data, masked out below)
@@ -552,23 +573,20 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
     }
   };
   // the next tile: the rest of this unit, else the first tile of the next
-  auto next_of = [&](const Tile& cur, bool& new_unit) {
-    Tile nxt = cur;
-    nxt.tj += 64;
-    new_unit = nxt.tj >= cur.j1;
-    if (new_unit) {
-      const int un = cur.u + int(gridDim.x);
-      if (un < nunits) nxt = unit_tile(un);
-      else nxt.u = nunits;  // none
+  auto next_of = [&](const Tile& cur) {
+    if (cur.tj + 64 < cur.j1) {
+      Tile nxt = cur;
+      nxt.tj += 64;
+      return nxt;
     }
-    return nxt;
+    return next_unit(cur);
   };
-  // products and streaming sums of one tile held in (kt, va, vb, sb). All
-  // 16-key groups are multiplied first (the two centroid blocks' chains
-  // interleaved, eight independent chains per wave), then one rescale test
-  // per tile and the exponentials. A full tile (64 keys of the unit) takes a
-  // branch-free path; the unit's last, partial tile masks the keys past its
-  // end. Both centroid blocks are always multiplied: a block without live
+  // products and streaming sums of one tile held in (kt, va, vb, sb), in two
+  // halves of 32 keys: both halves are multiplied first (the two centroid
+  // blocks' chains interleaved), then each half takes its own rescale of
+  // the running reference (branch-free) and its exponentials. A full tile
+  // (64 keys of the unit) takes a branch-free path; the unit's last, partial
+  // tile masks the keys past its end. Both centroid blocks are always multiplied: a block without live
   // centroids has zero operands and is never recorded.
   auto compute_impl = [&](auto full_tag, const Tile& cur, const __bf16* kt, const float* va,
                           const float* vb, const float* sb) {
@@ -580,72 +598,88 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
     const f32x4 seed[2] = {f32x4{-st[0], -st[0], -st[0], -st[0]},
                            f32x4{-st[1], -st[1], -st[1], -st[1]}};
     f32x4 acc[2][4];
+    // products of groups kb0, kb0 + 1
+    auto products = [&](int kb0) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (FULL || kb < ngrp) {
-        Frag<__bf16> a[KC];
-#pragma unroll
-        for (int k = 0; k < KC; ++k) a[k] = load8(kt + (kb * KC + k) * 512 + lane * 8);
-        acc[0][kb] = seed[0];
-        acc[1][kb] = seed[1];
-#pragma unroll
-        for (int k = 0; k < KC; ++k)
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            mma(acc[0][kb], a[k], bq[0][k][p]);
-            mma(acc[1][kb], a[k], bq[1][k][p]);
-          }
-      }
-    }
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      float tmax = mp[cb];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = kb0; kb < kb0 + 2; ++kb) {
         if (FULL || kb < ngrp) {
+          Frag<__bf16> a[KC];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (!FULL && kb * 16 + g * 4 + i >= nvalid) acc[cb][kb][i] = -__builtin_inff();
-            tmax = fmaxf(tmax, acc[cb][kb][i]);
-          }
+          for (int k = 0; k < KC; ++k) a[k] = load8(kt + (kb * KC + k) * 512 + lane * 8);
+          acc[0][kb] = seed[0];
+          acc[1][kb] = seed[1];
+#pragma unroll
+          for (int k = 0; k < KC; ++k)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              mma(acc[0][kb], a[k], bq[0][k][p]);
+              mma(acc[1][kb], a[k], bq[1][k][p]);
+            }
         }
       }
-      if (tmax > mp[cb]) {
-        const float al = fast_exp2(mp[cb] - tmax);
-        Z[cb] *= al;
-        E[cb] *= al * al;
-        if (VALUE) Ev[cb] *= al * al;
-        mp[cb] = tmax;
-        e2[cb] = fast_exp2(-tmax);
-      }
-      const float m = mp[cb], ee = e2[cb];
-      float zs[2] = {0.f, 0.f}, es[2] = {0.f, 0.f}, vs2[2] = {0.f, 0.f};
+    };
+    // rescale test and streamed sums of groups kb0, kb0 + 1
+    auto sums = [&](int kb0) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        if (FULL || kb < ngrp) {
-          float ax[4], bx[4];
-          if (VALUE) {
-            const float4 xa = *reinterpret_cast<const float4*>(va + kb * 16 + g * 4);
-            const float4 xb = *reinterpret_cast<const float4*>(vb + kb * 16 + g * 4);
-            ax[0] = xa.x; ax[1] = xa.y; ax[2] = xa.z; ax[3] = xa.w;
-            bx[0] = xb.x; bx[1] = xb.y; bx[2] = xb.z; bx[3] = xb.w;
-          }
+      for (int cb = 0; cb < 2; ++cb) {
+        float tmax = mp[cb];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // a masked key gives e = 0 and dd = -ee: its square is dropped
-            const int pp = i & 1;
-            const float e = fast_exp2(acc[cb][kb][i] - m);
-            zs[pp] += e;
-            const float dd = (FULL || kb * 16 + g * 4 + i < nvalid) ? e - ee : 0.f;
-            es[pp] = fmaf(dd, dd, es[pp]);
-            if (VALUE) vs2[pp] = fmaf(e, fmaf(dd, bx[i], e * ax[i]), vs2[pp]);
+        for (int kb = kb0; kb < kb0 + 2; ++kb) {
+          if (FULL || kb < ngrp) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (!FULL && kb * 16 + g * 4 + i >= nvalid) acc[cb][kb][i] = -__builtin_inff();
+              tmax = fmaxf(tmax, acc[cb][kb][i]);
+            }
           }
         }
+        // the reference follows the maximum without a branch (al = 1 when it
+        // stays), so that a full tile is one straight block of code
+        {
+          const float mn = fmaxf(mp[cb], tmax);
+          const float al = fast_exp2(mp[cb] - mn);
+          Z[cb] *= al;
+          E[cb] *= al * al;
+          if (VALUE) Ev[cb] *= al * al;
+          mp[cb] = mn;
+          e2[cb] = fast_exp2(-mn);
+        }
+        const float m = mp[cb], ee = e2[cb];
+        float zs[2] = {0.f, 0.f}, es[2] = {0.f, 0.f}, vs2[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kb = kb0; kb < kb0 + 2; ++kb) {
+          if (FULL || kb < ngrp) {
+            float ax[4], bx[4];
+            if (VALUE) {
+              const float4 xa = *reinterpret_cast<const float4*>(va + kb * 16 + g * 4);
+              const float4 xb = *reinterpret_cast<const float4*>(vb + kb * 16 + g * 4);
+              ax[0] = xa.x; ax[1] = xa.y; ax[2] = xa.z; ax[3] = xa.w;
+              bx[0] = xb.x; bx[1] = xb.y; bx[2] = xb.z; bx[3] = xb.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              // a masked key gives e = 0 and dd = -ee: its square is dropped
+              const int pp = i & 1;
+              const float e = fast_exp2(acc[cb][kb][i] - m);
+              zs[pp] += e;
+              const float dd = (FULL || kb * 16 + g * 4 + i < nvalid) ? e - ee : 0.f;
+              es[pp] = fmaf(dd, dd, es[pp]);
+              if (VALUE) vs2[pp] = fmaf(e, fmaf(dd, bx[i], e * ax[i]), vs2[pp]);
+            }
+          }
+        }
+        Z[cb] += zs[0] + zs[1];
+        E[cb] += es[0] + es[1];
+        if (VALUE) Ev[cb] += vs2[0] + vs2[1];
       }
-      Z[cb] += zs[0] + zs[1];
-      E[cb] += es[0] + es[1];
-      if (VALUE) Ev[cb] += vs2[0] + vs2[1];
-    }
+    };
+    // the second half's products overlap the first half's sums: in a full
+    // tile (one block of straight code) the scheduler is asked to alternate
+    // one matrix instruction with a few vector ones
+    products(0);
+    products(2);
+    sums(0);
+    sums(2);
   };
   auto compute = [&](const Tile& cur, const __bf16* kt, const float* va, const float* vb,
                      const float* sb) {
@@ -680,7 +714,7 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
   };
   // one step: wait for the current tile's copies (leaving the next tile's in
   // flight), start the copies two tiles ahead, multiply the current tile.
-  // cur, n1, n2 are the current tile and the next two (u == nunits: none);
+  // cur, n1, n2 are the current tile and the next two (u == kNone: none);
   // past the last tile the copies repeat the current one, so that every step
   // issues and waits for the same number of copies.
   // Returns false after the last tile.
@@ -694,29 +728,41 @@ __global__ __launch_bounds__(256) void probe_bf16_kernel(
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(n2.u < nunits ? n2 : cur, ktn, van, vbn, sbn);
+    issue(n2.u != kNone ? n2 : cur, ktn, van, vbn, sbn);
     compute(cur, kt, va, vb, sb);
-    if (n1.u >= nunits || n1.u != cur.u) {
+    if (n1.u != cur.u) {
       record(cur);
       reset();
     }
     cur = n1;
     n1 = n2;
-    if (n2.u < nunits) {
-      bool nu;
-      n2 = next_of(n2, nu);
-    }
-    return cur.u < nunits;
+    if (n2.u != kNone) n2 = next_of(n2);
+    return cur.u != kNone;
   };
 
-  Tile cur = unit_tile(blockIdx.x);
+  // the first unit: the one after the (possibly empty) stretch of the cluster
+  // holding key J0 that starts before J0
+  Tile cur;
+  {
+    int lo = 0, hi = Ck;  // the last cluster c with ko[c] <= J0 (a non-empty one)
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ko[mid] <= J0) lo = mid; else hi = mid;
+    }
+    const int k = (J0 - ko[lo] + kProbeUnit - 1) / kProbeUnit;  // units starting before J0
+    Tile before;
+    before.cc = lo;
+    before.kend = ko[lo + 1];
+    before.u = up[lo] + k - 1;
+    before.j0 = before.j1 = min(ko[lo] + k * kProbeUnit, before.kend);
+    cur = next_unit(before);
+  }
+  if (cur.u == kNone) return;  // uniform: no unit starts in this block's keys
   reset();
-  bool nu;
-  Tile n1 = next_of(cur, nu);
-  Tile n2 = n1;
-  if (n1.u < nunits) n2 = next_of(n1, nu);
+  Tile n1 = next_of(cur);
+  Tile n2 = n1.u != kNone ? next_of(n1) : n1;
   issue(cur, kt0, va0, vb0, sb0);
-  issue(n1.u < nunits ? n1 : cur, kt1, va1, vb1, sb1);
+  issue(n1.u != kNone ? n1 : cur, kt1, va1, vb1, sb1);
   while (step(cur, n1, n2, kt0, va0, vb0, sb0, kt2, va2, vb2, sb2) &&
          step(cur, n1, n2, kt1, va1, vb1, sb1, kt0, va0, vb0, sb0) &&
          step(cur, n1, n2, kt2, va2, vb2, sb2, kt1, va1, vb1, sb1)) {
@@ -786,6 +832,18 @@ size_t probe_ws_bytes(int H, int Nk, int Cq, int Ck, bool values) {
                  : 0);
 }
 
+// Blocks of 256 threads of `kernel` that the current device holds at once
+// (compute units times blocks per unit), or 0 on failure.
+static int resident_blocks(const void* kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
 template <typename T, int D, bool VALUE>
 static hipError_t probe_t(int H, int Nk, int Cq, int Ck, float sl2, const float* qc,
                           const void* Kp, const float* kc, const int32_t* koff, const int32_t* up,
@@ -796,16 +854,22 @@ static hipError_t probe_t(int H, int Nk, int Cq, int Ck, float sl2, const float*
   if (e != hipSuccess) return e;
   const int maxu = max_units(Nk, Ck);
   const int groups = ceil_div(Cq, kProbeGroup);
-  int per_head = ceil_div(2048, H * groups);
-  per_head = per_head < 1 ? 1 : (per_head > maxu ? maxu : per_head);
-  if constexpr (sizeof(T) == 2)
+  if constexpr (sizeof(T) == 2) {
+    // one wave of resident blocks: the head's keys split evenly over its blocks
+    const int cap = resident_blocks(reinterpret_cast<const void*>(&probe_bf16_kernel<D, VALUE>));
+    if (cap <= 0) return hipErrorInvalidDeviceFunction;
+    int per_head = cap / (H * groups);
+    per_head = per_head < 1 ? 1 : (per_head > maxu ? maxu : per_head);
     hipLaunchKernelGGL((probe_bf16_kernel<D, VALUE>), dim3(per_head, H, groups), dim3(256), 0, s,
                        qc, static_cast<const __bf16*>(Kp), koff, up, st2, vstat, Nk, Cq, Ck, maxu,
                        sl2, rec);
-  else
+  } else {
+    int per_head = ceil_div(2048, H * groups);
+    per_head = per_head < 1 ? 1 : (per_head > maxu ? maxu : per_head);
     hipLaunchKernelGGL((probe_kernel<T, D, VALUE>), dim3(per_head, H, groups), dim3(256), 0, s,
                        qc, static_cast<const T*>(Kp), kc, koff, up, st2, vstat, Nk, Cq, Ck, maxu,
                        sl2, rec);
+  }
   return hipGetLastError();
 }
 
