@@ -121,7 +121,12 @@ def test_argument_errors_return_before_any_launch(L):
                                  fake, 1 << 30, null) == 1
     assert L.svgear_route_global(1, 4, 4, fake, null, fake, 5, fake, null, null, null, null,
                                  fake, 1 << 30, null) == 1
-    assert L.svgear_route_global_workspace(2, 100, 500) == 2 * 100 * 500 * 16
+    # keys and indices, double-buffered, the sorted costs (int64), every
+    # block's sorted position, the per-tile digit counts (256 digits x 25 tiles
+    # of 2048 blocks) and the per-tile cost sums and minima
+    wsg = L.svgear_route_global_workspace(2, 100, 500)
+    need = 2 * 100 * 500 * 28 + 2 * 25 * 256 * 4
+    assert need <= wsg <= need + 4096
     assert L.svgear_route_global_workspace(2, 100, 1025) == 0
     assert L.svgear_route_global(1, 4, 4, fake, fake, fake, 5, fake, null, null, null, null,
                                  fake, 16, null) == 3
