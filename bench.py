@@ -360,7 +360,8 @@ def run(args, wl, q, k, v, iq, ik, qd, kd, vd, iqd, ikd):
         "attend": {"executed_block_tflops": exec_tflops,
                    "executed_block_frac_of_peak": exec_tflops / PEAK_BF16_TFLOPS,
                    "exact_tflop": exact / 1e12, "compensation_tflop": comp / 1e12},
-        "roofline": {"kernel": "attend_kernel<bf16,128>", "bound": "mfma",
+        "roofline": {"kernel": "attend_kernel<bf16,128> (256-query and short-tail launches)",
+                     "bound": "mfma",
                      "achieved": att_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": att_tflops / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic(wl.name)

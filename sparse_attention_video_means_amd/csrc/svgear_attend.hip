@@ -62,13 +62,30 @@ struct AttCfg<__bf16> {
   static constexpr int QB = 2;              // 16-query blocks per wavefront
   static constexpr int NW = SVGEAR_ATT_NW;  // wavefronts per block
   static constexpr int ROWS = 8192;         // packed key positions per source-row window
+  static constexpr int STAGES = 3;          // tile buffers (copies run STAGES - 1 tiles ahead)
 };
 template <>
 struct AttCfg<float> {
   static constexpr int QB = 1;
   static constexpr int NW = 4;
   static constexpr int ROWS = 1024;
+  static constexpr int STAGES = 2;
 };
+// The short last blocks of the query clusters (at most 128 queries): four
+// wavefronts, two tile buffers and a small source-row window, so that two
+// such blocks share a compute unit (a full-size block with few active
+// wavefronts holds a whole unit).
+struct AttTailCfg {
+  static constexpr int QB = 2;
+  static constexpr int NW = 4;
+  static constexpr int ROWS = 1024;
+  static constexpr int STAGES = 2;
+};
+// Which query tiles a launch covers: every tile of BM queries (kAllTiles);
+// the tiles of 256 queries except a last one of at most 128 (kFullTiles);
+// only those last ones (kShortTails).
+constexpr int kAllTiles = 0, kFullTiles = 1, kShortTails = 2;
+constexpr int kTailMax = 128;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -222,16 +239,16 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_kernel(
+template <typename T, int D, typename Cfg>
+__global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
     const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
     const int32_t* __restrict__ qoff, const int32_t* __restrict__ koff,
     const T* __restrict__ kcen, const T* __restrict__ vcen, const uint8_t* __restrict__ mask,
-    int H, int Nq, int Nk, int Cq, int Ck, float sl2, int per_head, int span,
+    int H, int Nq, int Nk, int Cq, int Ck, float sl2, int per_head, int span, int mode,
     const int32_t* __restrict__ qperm, T* __restrict__ Op) {
   using L = TileLayout<T, D>;
-  constexpr int QB = AttCfg<T>::QB;
-  constexpr int NW = AttCfg<T>::NW;
+  constexpr int QB = Cfg::QB;
+  constexpr int NW = Cfg::NW;
   constexpr int BM = 16 * NW * QB;
   constexpr int KC = D / 32;
   constexpr int DB = D / 16;
@@ -242,7 +259,8 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   constexpr int TILE = kAttBK * D;          // elements per tile
   // bf16 tiles are triple-buffered (copies run two tiles ahead); f32 tiles
   // are twice as large and double-buffered
-  constexpr int kStages = sizeof(T) == 2 ? 3 : 2;
+  constexpr int kStages = Cfg::STAGES;
+  static_assert(kStages == 2 || kStages == 3, "two or three tile buffers");
   constexpr int kAhead = kStages - 1;
   // two buffers per tensor as distinct objects: the compiler can then tell
   // the asynchronous fill of one from the reads of the other and inserts no
@@ -264,7 +282,7 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   float* cbias_s = reinterpret_cast<float*>(lists + 3 * Ck);  // ln |k_c'| / scale of those
   int* pref_s = lists + 4 * Ck;        // packed offset of every selected cluster (+ total)
   // source row of every packed exact key position in [rbase, rbase + ROWS)
-  __shared__ int rows_s[AttCfg<T>::ROWS];
+  __shared__ int rows_s[Cfg::ROWS];
   __shared__ int scratch[16];
   __shared__ int info[2];
 
@@ -280,10 +298,19 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   const int32_t* ko = koff + size_t(h) * (Ck + 1);
 
   // ---- which query cluster / tile this block owns
+  // (a cluster of n queries: n / 256 tiles of 256 and a last one of n % 256,
+  // split between the kFullTiles and kShortTails launches by its size)
+  auto tiles_of = [&](int n) {
+    if (mode == kAllTiles) return (n + BM - 1) / BM;
+    const int rem = n % 256;
+    const bool short_tail = rem > 0 && rem <= kTailMax;
+    if (mode == kFullTiles) return n / 256 + ((rem > 0 && !short_tail) ? 1 : 0);
+    return short_tail ? 1 : 0;
+  };
   int carry = 0;
   for (int b = 0; b < Cq; b += 64 * NW) {
     const int i = b + tid;
-    const int nt = (i < Cq) ? (qo[i + 1] - qo[i] + BM - 1) / BM : 0;
+    const int nt = (i < Cq) ? tiles_of(qo[i + 1] - qo[i]) : 0;
     int tot;
     const int ex = block_exclusive_scan(nt, scratch, &tot);
     if (nt > 0 && t >= carry + ex && t < carry + ex + nt) {
@@ -295,7 +322,7 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   if (t >= carry) return;  // uniform: every thread computed the same total
   __syncthreads();
   const int c = info[0];
-  const int q0 = qo[c] + info[1] * BM;
+  const int q0 = qo[c] + (mode == kShortTails ? (qo[c + 1] - qo[c]) / 256 * 256 : info[1] * BM);
   const int q1 = min(qo[c + 1], q0 + BM);
 
   // ---- selected (packed) and compensated key-cluster lists
@@ -338,7 +365,7 @@ __global__ __launch_bounds__(64 * AttCfg<T>::NW, 8 / AttCfg<T>::NW) void attend_
   // a time: wave w walks selected clusters w, w + NW, ... and its lanes write
   // consecutive positions (the keys of a selected cluster are consecutive rows
   // of the permuted tensors)
-  constexpr int ROWS = AttCfg<T>::ROWS;
+  constexpr int ROWS = Cfg::ROWS;
   static_assert(ROWS % kAttBK == 0, "windows hold whole tiles");
   int rbase = 0;
   auto fill_rows = [&](int base) {
@@ -634,20 +661,37 @@ size_t attend_ws_bytes(int elem_bytes, int H, int Ck, int d) {
   return elem_bytes == 4 ? 0 : 2 * align256(size_t(elem_bytes) * H * Ck * d);
 }
 
+template <typename T, int D, typename Cfg>
+static void attend_launch(int mode, int per_head, int H, int Nq, int Nk, int Cq, int Ck, float sl2,
+                          const void* Qp, const void* Kp, const void* Vp, const int32_t* qoff,
+                          const int32_t* koff, const void* kc, const void* vc,
+                          const uint8_t* mask, const int32_t* qperm, void* Op, hipStream_t s) {
+  const int span = ceil_div(H * per_head, kXcds);
+  const size_t lds_lists = sizeof(int) * (5 * size_t(Ck) + 1);
+  hipLaunchKernelGGL((attend_kernel<T, D, Cfg>), dim3(span * kXcds), dim3(64 * Cfg::NW), lds_lists,
+                     s, static_cast<const T*>(Qp), static_cast<const T*>(Kp),
+                     static_cast<const T*>(Vp), qoff, koff, static_cast<const T*>(kc),
+                     static_cast<const T*>(vc), mask, H, Nq, Nk, Cq, Ck, sl2, per_head, span,
+                     mode, qperm, static_cast<T*>(Op));
+}
+
 template <typename T, int D>
 static void attend_t(int H, int Nq, int Nk, int Cq, int Ck, float sl2, const void* Qp,
                      const void* Kp, const void* Vp, const int32_t* qoff, const int32_t* koff,
                      const void* kc, const void* vc, const uint8_t* mask,
                      const int32_t* qperm, void* Op, hipStream_t s) {
-  constexpr int BM = 16 * AttCfg<T>::NW * AttCfg<T>::QB;
-  const int per_head = ceil_div(Nq, BM) + Cq;  // upper bound on query tiles per head
-  const int span = ceil_div(H * per_head, kXcds);
-  const size_t lds_lists = sizeof(int) * (5 * size_t(Ck) + 1);
-  hipLaunchKernelGGL((attend_kernel<T, D>), dim3(span * kXcds), dim3(64 * AttCfg<T>::NW), lds_lists, s,
-                     static_cast<const T*>(Qp), static_cast<const T*>(Kp),
-                     static_cast<const T*>(Vp), qoff, koff, static_cast<const T*>(kc),
-                     static_cast<const T*>(vc), mask, H, Nq, Nk, Cq, Ck, sl2, per_head, span,
-                     qperm, static_cast<T*>(Op));
+  using C = AttCfg<T>;
+  constexpr int BM = 16 * C::NW * C::QB;
+  if constexpr (sizeof(T) == 2 && BM == 256) {
+    // blocks of 256 queries, then the short last blocks two to a compute unit
+    attend_launch<T, D, C>(kFullTiles, ceil_div(Nq, BM) + Cq, H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp,
+                           qoff, koff, kc, vc, mask, qperm, Op, s);
+    attend_launch<T, D, AttTailCfg>(kShortTails, Cq, H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp, qoff,
+                                    koff, kc, vc, mask, qperm, Op, s);
+  } else {
+    attend_launch<T, D, C>(kAllTiles, ceil_div(Nq, BM) + Cq, H, Nq, Nk, Cq, Ck, sl2, Qp, Kp, Vp,
+                           qoff, koff, kc, vc, mask, qperm, Op, s);
+  }
 }
 
 hipError_t launch_attend(int elem_bytes, int H, int Nq, int Nk, int d, int Cq, int Ck,
