@@ -82,8 +82,9 @@ ATTEND_SRC = os.path.join(ROOT, "sparse_attention_video_means_amd", "csrc", "svg
 
 
 def measured_traffic(workload):
-    """HBM bytes per attention launch from the committed counter summary, or
-    None when the kernel source or the workload differs from the profiled one."""
+    """HBM bytes of the attention stage (its two launches) from the committed
+    counter summary, or None when the kernel source or the workload differs
+    from the profiled one."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
@@ -92,7 +93,7 @@ def measured_traffic(workload):
         return None
     if rec.get("source_sha256") != sha or rec.get("workload") != workload:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_stage")
 
 
 def algorithmic_flops(ra, d):
