@@ -237,8 +237,9 @@ svgear_status svgear_route(int H, int Cq, int Ck, const float* ratio, const int3
 /*
  * Greedy error-to-cost routing under one budget for the whole attention map of
  * a head (paper §4.1: at most rho * Nq * Nk exact entries in the block mask;
- * §4.2: blocks with the highest error-to-size ratio first until the budget is
- * used). Unlike svgear_route, the budget is not split per query cluster.
+ * §4.2: blocks taken in decreasing order of estimated error per entry while
+ * the budget lasts). Unlike svgear_route, the budget is not split per query
+ * cluster.
  *
  * Every block (c, c') whose query cluster and key cluster are both non-empty
  * competes for `budget_entries` exact (query, key) entries and costs

@@ -1,5 +1,6 @@
-// Greedy error-to-cost routers (paper §4.2 "Error estimation": highest
-// error-to-size ratio first until the budget is exhausted).
+// Greedy error-to-cost routers (paper §4.2, error estimation: blocks are
+// taken in decreasing order of estimated error per entry while the budget
+// lasts).
 //
 // route_kernel: one block per (head, query cluster), a budget of exact keys
 // per query cluster (§5 "Implementation": routing per query cluster).
