@@ -120,10 +120,13 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ X,
       if (ob < best[tb] || (ob == best[tb] && oi < bidx[tb])) { best[tb] = ob; bidx[tb] = oi; }
     }
   }
-  // lane (g, r) now owns row row0 + 16 g + r = row0 + lane
+  // lane (g, r) now owns row row0 + 16 g + r = row0 + lane. (Padding
+  // centroids past C carry an infinite norm and never win; the clamp keeps
+  // the rank, the histogram and the scatter that reads them in range anyway.)
   int my = bidx[0];
 #pragma unroll
   for (int tb = 1; tb < 4; ++tb) my = (g == tb) ? bidx[tb] : my;
+  my = min(my, C - 1);
   const int n = row0 + lane;
   const bool valid = n < N;
   if (valid) labels[size_t(h) * N + n] = my;
