@@ -44,6 +44,8 @@
 // the end of the step. Each step ends with one wait (this wave's copies of
 // tile t+1) and one barrier. f32 tiles are twice as large and use two
 // buffers, one tile ahead.
+#include <type_traits>
+
 #include "svgear_common.hpp"
 #include "svgear_internal.hpp"
 
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
   // ---- which query cluster / tile this block owns
   // (a cluster of n queries: n / 256 tiles of 256 and a last one of n % 256,
   // split between the kFullTiles and kShortTails launches by its size)
-  auto tiles_of = [&](int n) {
+  auto tiles_of = [&](int n) __attribute__((always_inline)) {
     if (mode == kAllTiles) return (n + BM - 1) / BM;
     const int rem = n % 256;
     const bool short_tail = rem > 0 && rem <= kTailMax;
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
   constexpr int ROWS = Cfg::ROWS;
   static_assert(ROWS % kAttBK == 0, "windows hold whole tiles");
   int rbase = 0;
-  auto fill_rows = [&](int base) {
+  auto fill_rows = [&](int base) __attribute__((always_inline)) {
     for (int j = w; j < nsel; j += NW) {
       const int a = max(pref_s[j], base), b = min(pref_s[j + 1], base + ROWS);
       const int st = start_s[j];
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
   const size_t kv_bytes = size_t(Nk) * RB, cen_bytes = size_t(Ck) * RB;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   // sources of this lane's K and V rows of `tile`, its row bias, and the copies
-  auto issue = [&](int tile, T* kd, T* vd, float* bd) {
+  auto issue = [&](int tile, T* kd, T* vd, float* bd) __attribute__((always_inline)) {
     const bool exact = tile < nt_exact;  // uniform over the block
     int ksrc[NI], vsrc[NI];
     float bias;
@@ -438,18 +440,26 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
   // at [15:14])
   constexpr int kInFlight = (kAhead - 1) * 2 * NI;
   static_assert(kInFlight < 64, "vmcnt field");
-  auto wait_copies_but_newest = [&]() {
+  auto wait_copies_but_newest = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt((kInFlight & 15) | (7 << 4) | ((kInFlight >> 4) << 14));
   };
 
   // ---- Q^T fragments
   const T* Qh = Qp + size_t(h) * Nq * D;
-  const int qw = q0 + w * 16 * QB;
-  const bool active = qw < q1;
+  // query block qb of this wave: 16 rows from q0 + 16 (w + NW qb). Spread
+  // this way, a partial tile's blocks fall evenly on the SIMDs (wavefronts w
+  // and w + NW/2 share one), and a wave whose last block lies past the tile
+  // runs a loop without it (nq below).
+  auto qbase = [&](int qb) __attribute__((always_inline)) { return q0 + 16 * (w + NW * qb); };
+  const bool active = qbase(0) < q1;
+  int nq = 0;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) nq += (qbase(qb) < q1) ? 1 : 0;
+  nq = __builtin_amdgcn_readfirstlane(nq);
   Frag<T> qf[QB][KC];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qw + qb * 16 + r;
+    const int qi = qbase(qb) + r;
 #pragma unroll
     for (int k = 0; k < KC; ++k)
       qf[qb][k] = (qi < q1) ? load8(Qh + size_t(qi) * D + k * 32 + g * 8) : zero_frag<T>();
@@ -492,29 +502,33 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
     for (int db = 0; db < DB; ++db) va[db] = L::vt_frag(vb_s, kh, db, lane);
   };
   // S^T in raw logit units, accumulators seeded with the rows' biases
-  auto qk = [&](f32x4 (&sh)[2][QB], const Frag<T> (&ka)[2][KC], const float* bb_s, int kh) {
+  // (NQ: the number of this wave's query blocks, a compile-time constant)
+  auto qk = [&](auto NQ, f32x4 (&sh)[2][QB], const Frag<T> (&ka)[2][KC], const float* bb_s,
+                int kh) {
+    constexpr int nqc = decltype(NQ)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const f32x4 b4 = *reinterpret_cast<const f32x4*>(bb_s + kh * 32 + kb * 16 + g * 4);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sh[kb][qb] = b4;
+      for (int qb = 0; qb < nqc; ++qb) sh[kb][qb] = b4;
     }
 #pragma unroll
     for (int k = 0; k < KC; ++k)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mma(sh[kb][qb], ka[kb][k], qf[qb][k]);
+        for (int qb = 0; qb < nqc; ++qb) mma(sh[kb][qb], ka[kb][k], qf[qb][k]);
   };
   // raise the running maxima if a logit of the half exceeds its threshold;
   // l is scaled down to the new maximum at once and the factors are returned
   // for O (true if any is not 1), which the caller scales once every weight
   // computed under the old maxima has been added to it
-  auto check = [&](const f32x4 (&sh)[2][QB], float (&al)[QB]) -> bool {
+  auto check = [&](auto NQ, const f32x4 (&sh)[2][QB], float (&al)[QB]) -> bool {
+    constexpr int nqc = decltype(NQ)::value;
     float mx[QB];
     bool up = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < nqc; ++qb) {
       float m = sh[0][qb][0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) m = fmaxf(m, sh[e >> 2][qb][e & 3]);
@@ -523,7 +537,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
     }
     if (__ballot(up) == 0ull) return false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < nqc; ++qb) {
       const float mn = fmaxf(mrow[qb], quad_max(mx[qb]) * sl2);  // the scale is positive
       al[qb] = (mn > mrow[qb]) ? fast_exp2(mrow[qb] - mn) : 1.f;
       mrow[qb] = mn;
@@ -533,17 +547,19 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
     }
     return true;
   };
-  auto scale_o = [&](const float (&al)[QB]) {
+  auto scale_o = [&](auto NQ, const float (&al)[QB]) {
+    constexpr int nqc = decltype(NQ)::value;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < nqc; ++qb)
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db][qb] *= al[qb];
   };
   // P^T fragments and their sums (the denominator adds the same rounded
   // weights the numerator uses)
-  auto weights = [&](const f32x4 (&sh)[2][QB], Frag<T> (&pb)[QB]) {
+  auto weights = [&](auto NQ, const f32x4 (&sh)[2][QB], Frag<T> (&pb)[QB]) {
+    constexpr int nqc = decltype(NQ)::value;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < nqc; ++qb) {
       const float nm = -mrow[qb];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
@@ -552,17 +568,18 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
       else lsum[qb] = frag_sum(pb[qb], lsum[qb]);
     }
   };
-  auto pv = [&](const Frag<T> (&va)[DB], const Frag<T> (&pb)[QB]) {
+  auto pv = [&](auto NQ, const Frag<T> (&va)[DB], const Frag<T> (&pb)[QB]) {
+    constexpr int nqc = decltype(NQ)::value;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) mma(o[db][qb], va[db], pb[qb]);
+      for (int qb = 0; qb < nqc; ++qb) mma(o[db][qb], va[db], pb[qb]);
   };
 
   // copies of tile+kAhead into the buffer that tile-1 used. Past the last
   // tile the copies still run (filler rows), so that every step ends with
   // the same wait: all but this wave's newest copies.
-  auto copy_ahead = [&](int tile, T* kn_s, T* vn_s, float* bn_s) {
+  auto copy_ahead = [&](int tile, T* kn_s, T* vn_s, float* bn_s) __attribute__((always_inline)) {
     const int nxt = tile + kAhead;
     if (nxt < nt_exact && nxt * kAttBK == rbase + ROWS) {
       // the tile copied next starts a new window of source rows (every wave
@@ -576,8 +593,8 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
   // one tile. Two tiles ahead (bf16), the copies are issued after this
   // tile's matrix work, so that its first LDS reads start the step; one tile
   // ahead (f32), before it, so that they overlap it.
-  auto step = [&](int tile, const T* kb_s, const T* vb_s, const float* bb_s, T* kn_s, T* vn_s,
-                  float* bn_s) {
+  auto step = [&](auto NQ, int tile, const T* kb_s, const T* vb_s, const float* bb_s, T* kn_s,
+                  T* vn_s, float* bn_s) __attribute__((always_inline)) {
     if (kAhead == 1) copy_ahead(tile, kn_s, vn_s, bn_s);
     if (active && tile >= 0) {
       Frag<T> ka0[2][KC], ka1[2][KC], va0[DB], va1[DB], pb0[QB], pb1[QB];
@@ -585,17 +602,17 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
       kfrags(ka0, kb_s, 0);
       kfrags(ka1, kb_s, 1);
       float al0[QB], al1[QB];
-      qk(s0, ka0, bb_s, 0);
-      if (check(s0, al0)) scale_o(al0);
+      qk(NQ, s0, ka0, bb_s, 0);
+      if (check(NQ, s0, al0)) scale_o(NQ, al0);
       vfrags(va0, vb_s, 0);
-      qk(s1, ka1, bb_s, 1);
-      weights(s0, pb0);
-      const bool up1 = check(s1, al1);
+      qk(NQ, s1, ka1, bb_s, 1);
+      weights(NQ, s0, pb0);
+      const bool up1 = check(NQ, s1, al1);
       vfrags(va1, vb_s, 1);
-      pv(va0, pb0);             // weights of the old maxima first,
-      weights(s1, pb1);
-      if (up1) scale_o(al1);    // then O follows l to the new maxima
-      pv(va1, pb1);
+      pv(NQ, va0, pb0);             // weights of the old maxima first,
+      weights(NQ, s1, pb1);
+      if (up1) scale_o(NQ, al1);    // then O follows l to the new maxima
+      pv(NQ, va1, pb1);
     }
     if (kAhead > 1) copy_ahead(tile, kn_s, vn_s, bn_s);
     wait_copies_but_newest();
@@ -607,19 +624,29 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
   // destinations the compiler tells apart (it then inserts no wait between
   // the copies into one buffer and the reads of another). The guards are
   // nested so that no path reaches a step without the one before it.
-  if constexpr (kStages == 3) {
-    for (int tile = -2; tile < nt_all; tile += 3) {
-      step(tile, ks1, vs1, bias1, ks0, vs0, bias0);
-      if (tile + 1 < nt_all) {
-        step(tile + 1, ks2, vs2, bias2, ks1, vs1, bias1);
-        if (tile + 2 < nt_all) step(tile + 2, ks0, vs0, bias0, ks2, vs2, bias2);
+  // one copy of the loop per query-block count, so that a wave without its
+  // last block runs no matrix or vector work for it
+  auto run = [&](auto NQ) __attribute__((always_inline)) {
+    if constexpr (kStages == 3) {
+      for (int tile = -2; tile < nt_all; tile += 3) {
+        step(NQ, tile, ks1, vs1, bias1, ks0, vs0, bias0);
+        if (tile + 1 < nt_all) {
+          step(NQ, tile + 1, ks2, vs2, bias2, ks1, vs1, bias1);
+          if (tile + 2 < nt_all) step(NQ, tile + 2, ks0, vs0, bias0, ks2, vs2, bias2);
+        }
+      }
+    } else {
+      for (int tile = -1; tile < nt_all; tile += 2) {
+        step(NQ, tile, ks1, vs1, bias1, ks0, vs0, bias0);
+        if (tile + 1 < nt_all) step(NQ, tile + 1, ks0, vs0, bias0, ks1, vs1, bias1);
       }
     }
+  };
+  if constexpr (QB > 1) {
+    if (nq < QB) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, QB>{});
   } else {
-    for (int tile = -1; tile < nt_all; tile += 2) {
-      step(tile, ks1, vs1, bias1, ks0, vs0, bias0);
-      if (tile + 1 < nt_all) step(tile + 1, ks0, vs0, bias0, ks1, vs1, bias1);
-    }
+    run(std::integral_constant<int, 1>{});
   }
   // the filler copies of the last steps land before the block's LDS is freed
   __builtin_amdgcn_s_waitcnt(0);
@@ -631,8 +658,9 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
   const int32_t* ph = qperm ? qperm + size_t(h) * Nq : nullptr;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    if (qb >= nq) break;
     const float inv = 1.f / (kOnesSum ? lacc[qb][0] : quad_sum(lsum[qb]));
-    const int qp = qw + qb * 16 + r;
+    const int qp = qbase(qb) + r;
     const int qi = (ph && qp < q1) ? ph[qp] : qp;
     if (qp < q1 && unsigned(qi) < unsigned(Nq)) {
 #pragma unroll
