@@ -3,7 +3,9 @@
 // exact keys of its selected key clusters and one centroid logit (+ ln|k_c'|)
 // per skipped non-empty key cluster, with mean values for the latter.
 //
-// Block = NW wavefronts x (16*QB) queries of one query cluster. The selected
+// Block = NW wavefronts x (16*QB) queries of one query cluster; wavefront w
+// takes the 16-query groups w, w + NW, ..., so that a partial block's groups
+// spread evenly over the SIMDs. The selected
 // key clusters are packed back to back into 64-key tiles (a tile may span
 // several clusters, so ragged cluster ends waste no matrix work); the skipped
 // clusters' centroid rows (pre-rounded to the element type) follow as further
