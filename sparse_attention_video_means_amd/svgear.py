@@ -143,6 +143,16 @@ def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _user_ws(ws, nbytes: int, device) -> torch.Tensor:
+    """The caller's workspace, if one is given (a dense uint8 tensor on the
+    call's device; replaced by a new one when smaller than ``nbytes``), else
+    a new one."""
+    if ws is None:
+        return _ws(nbytes, device)
+    _need(ws, "ws", torch.uint8, None, device)
+    return ws if ws.numel() >= nbytes else _ws(nbytes, device)
+
+
 # ----------------------------------------------------------------------------
 def svgear_cluster(x: torch.Tensor, centroids: torch.Tensor, iters: int, ws=None):
     """k-means of every head's rows; ``centroids`` ([H, C, d] f32) is updated in
@@ -154,9 +164,7 @@ def svgear_cluster(x: torch.Tensor, centroids: torch.Tensor, iters: int, ws=None
     labels = torch.empty((H, N), dtype=torch.int32, device=x.device)
     counts = torch.empty((H, C), dtype=torch.int32, device=x.device)
     L = lib()
-    nbytes = L.svgear_cluster_workspace(_dt(x), H, N, d, C)
-    if ws is None or ws.numel() < nbytes:
-        ws = _ws(nbytes, x.device)
+    ws = _user_ws(ws, L.svgear_cluster_workspace(_dt(x), H, N, d, C), x.device)
     _check("svgear_cluster", L.svgear_cluster(_dt(x), H, N, d, C, int(iters), _ptr(x),
                                               _ptr(centroids), _ptr(labels), _ptr(counts),
                                               _ptr(ws), ws.numel(), _stream()))
@@ -183,9 +191,7 @@ def svgear_permute(labels: torch.Tensor, C: int, tensors, with_means: bool = Tru
     dst = (ctypes.c_void_p * nt)(*[t.data_ptr() for t in outs])
     mp = (ctypes.c_void_p * nt)(*[m.data_ptr() for m in means]) if with_means else None
     L = lib()
-    nbytes = L.svgear_permute_workspace(_dt(x0), H, N, d, C)
-    if ws is None or ws.numel() < nbytes:
-        ws = _ws(nbytes, dev)
+    ws = _user_ws(ws, L.svgear_permute_workspace(_dt(x0), H, N, d, C), dev)
     _check("svgear_permute", L.svgear_permute(_dt(x0), H, N, d, C, _ptr(labels), _ptr(perm),
                                               _ptr(offsets), nt, src, dst, mp, _ptr(ws),
                                               ws.numel(), _stream()))
@@ -216,9 +222,7 @@ def svgear_cluster_permute(tensors, centroids: torch.Tensor, iters: int, with_me
     dst = (ctypes.c_void_p * nt)(*[t.data_ptr() for t in outs])
     mp = (ctypes.c_void_p * nt)(*[m.data_ptr() for m in means]) if with_means else None
     L = lib()
-    nbytes = L.svgear_cluster_permute_workspace(_dt(x0), H, N, d, C)
-    if ws is None or ws.numel() < nbytes:
-        ws = _ws(nbytes, dev)
+    ws = _user_ws(ws, L.svgear_cluster_permute_workspace(_dt(x0), H, N, d, C), dev)
     _check("svgear_cluster_permute", L.svgear_cluster_permute(
         _dt(x0), H, N, d, C, int(iters), nt, src, dst, mp, _ptr(centroids), _ptr(labels),
         _ptr(counts), _ptr(perm), _ptr(offsets), _ptr(ws), ws.numel(), _stream()))
@@ -236,9 +240,7 @@ def svgear_probe(q_centroids, kp, k_centroids, k_offsets, scale: float, ws=None)
     ratio = torch.empty((H, Cq, Ck), dtype=torch.float32, device=kp.device)
     log_norm = torch.empty((H, Cq), dtype=torch.float32, device=kp.device)
     L = lib()
-    nbytes = L.svgear_probe_workspace(H, Nk, Cq, Ck)
-    if ws is None or ws.numel() < nbytes:
-        ws = _ws(nbytes, kp.device)
+    ws = _user_ws(ws, L.svgear_probe_workspace(H, Nk, Cq, Ck), kp.device)
     _check("svgear_probe", L.svgear_probe(_dt(kp), H, Nk, d, Cq, Ck, float(scale),
                                           _ptr(q_centroids), _ptr(kp), _ptr(k_centroids),
                                           _ptr(k_offsets), _ptr(ratio), _ptr(log_norm), _ptr(ws),
@@ -260,9 +262,7 @@ def svgear_probe_values(q_centroids, kp, k_centroids, vp, v_centroids, k_offsets
     ratio = torch.empty((H, Cq, Ck), dtype=torch.float32, device=kp.device)
     log_norm = torch.empty((H, Cq), dtype=torch.float32, device=kp.device)
     L = lib()
-    nbytes = L.svgear_probe_values_workspace(H, Nk, Cq, Ck)
-    if ws is None or ws.numel() < nbytes:
-        ws = _ws(nbytes, kp.device)
+    ws = _user_ws(ws, L.svgear_probe_values_workspace(H, Nk, Cq, Ck), kp.device)
     _check("svgear_probe_values", L.svgear_probe_values(
         _dt(kp), H, Nk, d, Cq, Ck, float(scale), _ptr(q_centroids), _ptr(kp), _ptr(k_centroids),
         _ptr(vp), _ptr(v_centroids), _ptr(k_offsets), _ptr(ratio), _ptr(log_norm), _ptr(ws),
@@ -310,8 +310,7 @@ def svgear_route_global(ratio, q_offsets, k_offsets, budget_entries: int, ws=Non
     keys = torch.empty((H, Cq), dtype=torch.int32, device=dev)
     used = torch.empty((H,), dtype=torch.int64, device=dev)
     L = lib()
-    if ws is None:
-        ws = _ws(L.svgear_route_global_workspace(H, Cq, Ck), dev)
+    ws = _user_ws(ws, L.svgear_route_global_workspace(H, Cq, Ck), dev)
     _check("svgear_route_global", L.svgear_route_global(
         H, Cq, Ck, _ptr(ratio), _ptr(q_offsets), _ptr(k_offsets), int(budget_entries),
         _ptr(mask), _ptr(lst), _ptr(cnt), _ptr(keys), _ptr(used), _ptr(ws), ws.numel(),
@@ -334,7 +333,7 @@ def svgear_attend(qp, kp, vp, q_offsets, k_offsets, k_centroids, v_centroids, se
     _need(v_centroids, "v_centroids", torch.float32, (H, Ck, d))
     _need(sel_mask, "sel_mask", torch.uint8, (H, Cq, Ck))
     op = torch.empty_like(qp) if out is None else out
-    _need(op, "out", qp.dtype, qp.shape)
+    _need(op, "out", qp.dtype, qp.shape, qp.device)
     L = lib()
     ws = _ws(L.svgear_attend_workspace(_dt(qp), H, Ck, d), qp.device)
     _check("svgear_attend", L.svgear_attend(_dt(qp), H, Nq, Nk, d, Cq, Ck, float(scale),
@@ -362,7 +361,7 @@ def svgear_attend_unpermute(qp, kp, vp, q_offsets, k_offsets, k_centroids, v_cen
     _need(sel_mask, "sel_mask", torch.uint8, (H, Cq, Ck))
     _need(q_perm, "q_perm", torch.int32, (H, Nq))
     o = torch.empty_like(qp) if out is None else out
-    _need(o, "out", qp.dtype, qp.shape)
+    _need(o, "out", qp.dtype, qp.shape, qp.device)
     L = lib()
     ws = _ws(L.svgear_attend_workspace(_dt(qp), H, Ck, d), qp.device)
     _check("svgear_attend_unpermute", L.svgear_attend_unpermute(
@@ -389,7 +388,7 @@ def svgear_attend_unpermute_noalloc(qp, kp, vp, q_offsets, k_offsets, k_centroid
     _need(v_centroids, "v_centroids", torch.float32, (H, Ck, d))
     _need(sel_mask, "sel_mask", torch.uint8, (H, Cq, Ck))
     _need(q_perm, "q_perm", torch.int32, (H, Nq))
-    _need(out, "out", qp.dtype, qp.shape)
+    _need(out, "out", qp.dtype, qp.shape, qp.device)
     _check("svgear_attend_unpermute_noalloc", lib().svgear_attend_unpermute_noalloc(
         _dt(qp), H, Nq, Nk, d, Cq, Ck, float(scale), _ptr(qp), _ptr(kp), _ptr(vp),
         _ptr(q_offsets), _ptr(k_offsets), _ptr(k_centroids), _ptr(v_centroids), _ptr(sel_mask),
@@ -403,6 +402,7 @@ def svgear_unpermute(xp, perm, out=None):
     H, N, d = xp.shape
     _need(perm, "perm", torch.int32, (H, N))
     x = torch.empty_like(xp) if out is None else out
+    _need(x, "out", xp.dtype, xp.shape, xp.device)
     _check("svgear_unpermute", lib().svgear_unpermute(_dt(xp), H, N, d, _ptr(perm), _ptr(xp),
                                                       _ptr(x), _stream()))
     return x
