@@ -448,10 +448,10 @@ __global__ __launch_bounds__(64 * Cfg::NW, 8 / Cfg::NW) void attend_kernel(
 
   // ---- Q^T fragments
   const T* Qh = Qp + size_t(h) * Nq * D;
-  // query block qb of this wave: 16 rows from q0 + 16 (w + NW qb). Spread
-  // this way, a partial tile's blocks fall evenly on the SIMDs (wavefronts w
-  // and w + NW/2 share one), and a wave whose last block lies past the tile
-  // runs a loop without it (nq below).
+  // query group qb of this wave: 16 rows from q0 + 16 (w + NW qb). The
+  // wavefronts of a block are dealt to the SIMDs in turn (w and w + NW/2 share
+  // one), so spread this way a partial tile's groups load the SIMDs evenly; a
+  // wave whose last group lies past the tile runs a loop without it (nq).
   auto qbase = [&](int qb) __attribute__((always_inline)) { return q0 + 16 * (w + NW * qb); };
   const bool active = qbase(0) < q1;
   int nq = 0;
