@@ -99,8 +99,10 @@ __device__ __forceinline__ int find_unit_cluster(const int32_t* prefix, int C, i
   return lo;
 }
 
-// (a_j, b_j) = (||v_j - vbar||^2, 2 (v_j - vbar).vbar) for every permuted key j,
-// 16 lanes per key row, 16 rows per block.
+// (a_j, b_j) = (||v_j - vbar||^2, 2 (v_j - vbar).vbar) for every permuted key j.
+// One block per key cluster, whose keys are the consecutive rows
+// [koff[c], koff[c+1]) of the permuted tensor: its mean row stays in
+// registers, 16 lanes per key row, 16 rows per pass.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void value_stats_kernel(const T* __restrict__ Vp,
                                                           const float* __restrict__ vc,
@@ -108,32 +110,31 @@ __global__ __launch_bounds__(256) void value_stats_kernel(const T* __restrict__ 
                                                           int Nk, int Ck,
                                                           float2* __restrict__ stats) {
   constexpr int EL = D / 16;  // elements per lane
-  const int h = blockIdx.y, tid = threadIdx.x, sub = tid & 15;
-  const int j = blockIdx.x * 16 + (tid >> 4);
-  const bool ok = j < Nk;
-  const int jj = ok ? j : Nk - 1;
+  const int h = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, sub = tid & 15;
   const int32_t* ko = koff + size_t(h) * (Ck + 1);
-  int lo = 0, hi = Ck;  // the key cluster holding permuted key jj
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (ko[mid] <= jj) lo = mid; else hi = mid;
-  }
-  const T* v = Vp + (size_t(h) * Nk + jj) * D + sub * EL;
-  const float* vb = vc + (size_t(h) * Ck + lo) * D + sub * EL;
-  float a = 0.f, b = 0.f;
+  const int j0 = max(ko[c], 0), j1 = min(ko[c + 1], Nk);
+  const float* vb = vc + (size_t(h) * Ck + c) * D + sub * EL;
+  float m[EL];
 #pragma unroll
-  for (int e = 0; e < EL; ++e) {
-    const float m = vb[e];
-    const float df = to_f32(v[e]) - m;
-    a = fmaf(df, df, a);
-    b = fmaf(df, m, b);
-  }
+  for (int e = 0; e < EL; ++e) m[e] = vb[e];
+  // (every lane of a 16-lane row group takes the same trip count, so the
+  // group's lane swaps below only read lanes of that group)
+  for (int j = j0 + (tid >> 4); j < j1; j += 16) {
+    const T* v = Vp + (size_t(h) * Nk + j) * D + sub * EL;
+    float a = 0.f, b = 0.f;
 #pragma unroll
-  for (int o = 8; o > 0; o >>= 1) {
-    a += __shfl_xor(a, o, 64);
-    b += __shfl_xor(b, o, 64);
+    for (int e = 0; e < EL; ++e) {
+      const float df = to_f32(v[e]) - m[e];
+      a = fmaf(df, df, a);
+      b = fmaf(df, m[e], b);
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      a += __shfl_xor(a, o, 64);
+      b += __shfl_xor(b, o, 64);
+    }
+    if (sub == 0) stats[size_t(h) * Nk + j] = make_float2(a, 2.f * b);
   }
-  if (ok && sub == 0) stats[size_t(h) * Nk + j] = make_float2(a, 2.f * b);
 }
 
 // w[h][k] = ||vbar_k||^2, one wavefront per key cluster.
@@ -876,7 +877,7 @@ static hipError_t probe_t(int H, int Nk, int Cq, int Ck, float sl2, const float*
 template <typename T, int D>
 static hipError_t value_stats_t(int H, int Nk, int Ck, const void* Vp, const float* vc,
                                 const int32_t* koff, float2* stats, float* wv, hipStream_t s) {
-  hipLaunchKernelGGL((value_stats_kernel<T, D>), dim3(ceil_div(Nk, 16), H), dim3(256), 0, s,
+  hipLaunchKernelGGL((value_stats_kernel<T, D>), dim3(Ck, H), dim3(256), 0, s,
                      static_cast<const T*>(Vp), vc, koff, Nk, Ck, stats);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
