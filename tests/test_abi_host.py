@@ -215,3 +215,31 @@ def test_routed_attention_checks_its_inputs_before_any_launch():
         return
     with pytest.raises(ValueError, match="q"):
         ra.check_inputs(**dict(good, q=good["q"].cuda()))   # another device
+
+
+def test_header_compiles_as_c_and_the_library_links_from_c(tmp_path):
+    """include/svgear.h is a C header: a C99 program (-Wall -Wextra -pedantic
+    -Werror) includes it, links libsvgear.so and calls it (host side only)."""
+    import shutil
+    import subprocess
+    from sparse_attention_video_means_amd import svgear
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    if os.environ.get("SVGEAR_LIB"):
+        # another build of the library (the sanitizer-instrumented one needs
+        # its runtime to link a program): this check is about the header
+        pytest.skip("SVGEAR_LIB names another build")
+    if not os.path.exists(svgear.LIB_PATH):
+        from sparse_attention_video_means_amd import build
+        build.build()
+    exe = str(tmp_path / "abi_from_c")
+    libdir = os.path.dirname(svgear.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "c_abi", "abi_from_c.c"), "-o", exe,
+                        svgear.LIB_PATH, "-Wl,-rpath," + libdir],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0, r.stdout
+    r = subprocess.run([exe], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0 and "abi from C: ok" in r.stdout, r.stdout
