@@ -60,3 +60,37 @@ def test_unpermute_output_of_the_wrong_shape_is_refused():
     back = S.svgear_unpermute(xp, perm, out=torch.empty_like(x))
     torch.cuda.synchronize()
     assert torch.equal(back, x)
+
+
+def test_optional_outputs_may_be_null():
+    """svgear_route's list, count and keys and svgear_probe's log normalisers
+    are optional: with NULL for them the required outputs are bitwise what a
+    call that asks for everything writes."""
+    import ctypes
+    import math
+
+    from sparse_attention_video_means_amd import synth
+    S = sv()
+    wl = synth.WORKLOADS["tiny"]
+    q, k, v = synth.make_qkv(wl)
+    iq = synth.kmeans_init(q, wl.cq, wl.seed, 0)
+    ik = synth.kmeans_init(k, wl.ck, wl.seed, 1)
+    scale = 1 / math.sqrt(wl.d)
+    res = S.routed_attention(q.to(DEV), k.to(DEV), v.to(DEV), wl.cq, wl.ck, wl.budget, wl.iters,
+                             iq.to(DEV), ik.to(DEV), scale)
+    L, s, p = S.lib(), S._stream(), S._ptr
+    H, Cq, Ck = res["ratio"].shape
+    mask = torch.empty_like(res["sel_mask"])
+    S._check("svgear_route", L.svgear_route(H, Cq, Ck, p(res["ratio"]), p(res["q_off"]),
+                                            p(res["k_off"]), int(wl.budget), p(mask), None,
+                                            None, None, None, 0, s))
+    kp, Nk = res["kp"], res["kp"].shape[1]
+    ratio = torch.empty_like(res["ratio"])
+    ws = S._ws(L.svgear_probe_workspace(H, Nk, Cq, Ck), kp.device)
+    S._check("svgear_probe", L.svgear_probe(S._dt(kp), H, Nk, wl.d, Cq, Ck, ctypes.c_float(scale),
+                                            p(res["q_bar"]), p(kp), p(res["k_bar"]),
+                                            p(res["k_off"]), p(ratio), None, p(ws), ws.numel(),
+                                            s))
+    torch.cuda.synchronize()
+    assert torch.equal(mask, res["sel_mask"])
+    assert torch.equal(ratio, res["ratio"])
