@@ -27,6 +27,10 @@ Protocol:
     count and BLAS configuration; `oracle_routing`: the oracle's probe and
     router on the GPU's labels for heads 0 and 1 (selection flips and
     exact-entry densities);
+  * `attend.frac_of_peak_at_measured_clock`: the attention rate against the
+    bf16 matrix peak at the shader clock the chip holds under matrix load
+    (the library's clock probe, run once per line), beside `roofline.frac`
+    against the published 2.5 PFLOP/s;
   * `--sweep stress` prints one such line per routing-stress point.
 """
 import argparse
@@ -79,6 +83,27 @@ EVICT_BYTES = 512 << 20  # written between the per-stage reps (twice the 256 MB 
 DENSE_REPS = 5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_wan22_traffic.json")
 ATTEND_SRC = os.path.join(ROOT, "sparse_attention_video_means_amd", "csrc", "svgear_attend.hip")
+
+
+def measured_clock():
+    """The shader clock while every matrix core is busy (the library's clock
+    probe: 8 blocks of four MFMA wavefronts per compute unit; the timed
+    wavefront runs ~1 ms) and the bf16 matrix peak at that clock, 4096 flops
+    per clock per compute unit (four SIMDs, a 16x16x32 MFMA every 16 clocks
+    each)."""
+    import torch
+
+    from sparse_attention_video_means_amd import svgear
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 8 * cus
+    svgear.svgear_clock_probe(blocks, 256)
+    out = svgear.svgear_clock_probe(blocks, 16384)
+    torch.cuda.synchronize()
+    o = out.cpu().tolist()
+    khz = svgear.svgear_realtime_khz()
+    mhz = (o[1] - o[0]) / (o[3] - o[2]) * khz / 1e3
+    return {"mhz": mhz, "compute_units": cus, "probe_ms": (o[3] - o[2]) / khz,
+            "bf16_peak_tflops": cus * 4096 * mhz * 1e6 / 1e12}
 
 
 def measured_traffic(workload):
@@ -323,6 +348,9 @@ def run(args, wl, q, k, v, iq, ik, qd, kd, vd, iqd, ikd):
         torch.cuda.synchronize()
         del src, dst
 
+    clock = measured_clock()
+    print(f"[bench] shader clock under matrix load: {clock}", file=sys.stderr, flush=True)
+
     cpu, check = None, None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on head 0", file=sys.stderr, flush=True)
@@ -360,7 +388,12 @@ def run(args, wl, q, k, v, iq, ik, qd, kd, vd, iqd, ikd):
         "densities": densities(ra, wl.n),
         "attend": {"executed_block_tflops": exec_tflops,
                    "executed_block_frac_of_peak": exec_tflops / PEAK_BF16_TFLOPS,
-                   "exact_tflop": exact / 1e12, "compensation_tflop": comp / 1e12},
+                   "exact_tflop": exact / 1e12, "compensation_tflop": comp / 1e12,
+                   "measured_clock_mhz": clock["mhz"],
+                   "bf16_peak_tflops_at_measured_clock": clock["bf16_peak_tflops"],
+                   "frac_of_peak_at_measured_clock": att_tflops / clock["bf16_peak_tflops"],
+                   "executed_block_frac_at_measured_clock":
+                       exec_tflops / clock["bf16_peak_tflops"]},
         "roofline": {"kernel": "attend_kernel<bf16,128> (256-query and short-tail launches)",
                      "bound": "mfma",
                      "achieved": att_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -420,6 +420,30 @@ svgear_status svgear_row_spread(svgear_dtype dt, int H, int N, int d, int C, con
                                 const float* means, const int32_t* offsets, float* spread,
                                 svgear_stream_t s);
 
+/*
+ * Measurement helpers (not part of the method): the shader clock the chip
+ * holds while its matrix cores are busy, so that a kernel's fraction of the
+ * bf16 matrix peak can also be taken at the clock it actually ran at (the
+ * nominal 2.4 GHz drops under matrix load).
+ *
+ * svgear_clock_probe enqueues `blocks` blocks of four wavefronts, each
+ * running `iters` rounds of eight independent bf16 16x16x32 MFMA chains on
+ * register operands (no memory traffic). The first wavefront of block 0
+ * reads the shader clock counter and the constant-rate real-time counter
+ * before and after its chains. Enough blocks to fill the GPU (8 per compute
+ * unit) keep every matrix core busy meanwhile.
+ *   out  device buffer of at least 4 + blocks uint64 words:
+ *        out[0], out[1]  shader clock counter at start and end (cycles),
+ *        out[2], out[3]  real-time counter at start and end (ticks),
+ *        out[4 + b]      a checksum of block b's products (bits of a float).
+ *   blocks, iters in [1, 2^20], out not NULL: else SVGEAR_ERR_INVALID_ARG.
+ * svgear_realtime_khz writes the real-time counter's rate for the current
+ * device (kHz). The clock in MHz is
+ *   (out[1] - out[0]) / (out[3] - out[2]) * khz / 1000.
+ */
+svgear_status svgear_clock_probe(int blocks, int iters, uint64_t* out, svgear_stream_t s);
+svgear_status svgear_realtime_khz(int* khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -519,4 +519,24 @@ svgear_status svgear_row_spread(svgear_dtype dt_in, int H, int N, int d, int C, 
   return SVGEAR_OK;
 }
 
+svgear_status svgear_clock_probe(int blocks, int iters, uint64_t* out, svgear_stream_t s) {
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20) || !out)
+    return SVGEAR_ERR_INVALID_ARG;
+  SVG_NEED_DEVICE();
+  SVG_TRY(launch_clock_probe(blocks, iters, out, as_stream(s)));
+  return SVGEAR_OK;
+}
+
+svgear_status svgear_realtime_khz(int* khz) {
+  if (!khz) return SVGEAR_ERR_INVALID_ARG;
+  SVG_NEED_DEVICE();
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || *khz <= 0) {
+    (void)hipGetLastError();
+    return SVGEAR_ERR_HIP;
+  }
+  return SVGEAR_OK;
+}
+
 }  // extern "C"

@@ -105,4 +105,7 @@ hipError_t launch_block_scores(int H, int d, int Cq, int Ck, float scale, const 
 hipError_t launch_row_spread(int elem_bytes, int H, int N, int d, int C, const void* Xp,
                              const float* mu, const int32_t* off, float* d2, hipStream_t s);
 
+// clock.hip
+hipError_t launch_clock_probe(int blocks, int iters, uint64_t* out, hipStream_t s);
+
 }  // namespace svg

@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
             "svgear_block_scores": (i32, [i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]),
             "svgear_map_error_workspace": (sz, [i32, i32, i32]),
             "svgear_row_spread": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+            "svgear_clock_probe": (i32, [i32, i32, vp, vp]),
+            "svgear_realtime_khz": (i32, [ctypes.POINTER(i32)]),
             "svgear_map_error": (i32, [i32, i32, i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp,
                                        vp, i32, vp, vp, vp, vp, sz, vp]),
         }
@@ -96,7 +98,7 @@ EXPORTS = ("svgear_status_string", "svgear_cluster_workspace", "svgear_cluster",
            "svgear_attend_workspace", "svgear_attend", "svgear_attend_unpermute",
            "svgear_attend_unpermute_noalloc", "svgear_unpermute",
            "svgear_block_scores", "svgear_map_error_workspace", "svgear_map_error",
-           "svgear_row_spread")
+           "svgear_row_spread", "svgear_clock_probe", "svgear_realtime_khz")
 
 
 def _check(fn: str, code: int):
@@ -589,6 +591,23 @@ def svgear_row_spread(xp, means, offsets):
                                                         _ptr(means), _ptr(offsets), _ptr(out),
                                                         _stream()))
     return out
+
+
+def svgear_clock_probe(blocks: int, iters: int, device="cuda"):
+    """Enqueue the clock probe; returns its [4 + blocks] int64 output buffer
+    (shader clock at start and end, real-time counter at start and end, then
+    one checksum per block), valid once the stream has reached it."""
+    out = torch.zeros(4 + int(blocks), dtype=torch.int64, device=device)
+    _check("svgear_clock_probe", lib().svgear_clock_probe(int(blocks), int(iters), _ptr(out),
+                                                          _stream()))
+    return out
+
+
+def svgear_realtime_khz() -> int:
+    """Rate of the real-time counter that svgear_clock_probe reads (kHz)."""
+    khz = ctypes.c_int(0)
+    _check("svgear_realtime_khz", lib().svgear_realtime_khz(ctypes.byref(khz)))
+    return khz.value
 
 
 def routed_attention(q, k, v, cq: int, ck: int, budget: int, iters: int, init_q, init_k,

@@ -108,6 +108,12 @@ def test_argument_errors_return_before_any_launch(L):
         L.svgear_probe_workspace(40, 75600, 100, 500)
     assert L.svgear_probe_values(1, 1, 100, 64, 4, 4, 0.1, fake, fake, fake, fake, fake, fake,
                                  fake, null, fake, 16, null) == 3
+    # clock probe: block and round counts out of range, null output
+    assert L.svgear_clock_probe(0, 10, fake, null) == 1
+    assert L.svgear_clock_probe(8, 0, fake, null) == 1
+    assert L.svgear_clock_probe((1 << 20) + 1, 10, fake, null) == 1
+    assert L.svgear_clock_probe(8, 10, null, null) == 1
+    assert L.svgear_realtime_khz(null) == 1
     # analysis: bad head dimension, short workspace, null output
     assert L.svgear_row_spread(1, 1, 100, 64, 4, fake, fake, fake, null, null) == 1
     assert L.svgear_block_scores(1, 96, 4, 4, 0.1, fake, fake, fake, fake, null) == 1
