@@ -237,39 +237,53 @@ struct FPtr3 {
   float* p[3];
 };
 
+// One wavefront per cluster (four per block), each lane holding dims lane and
+// lane + 64: the chunk sums of a dim are added in chunk order as before, and
+// ||round(mean)||^2 is the same two 64-lane shuffle trees added in the same
+// order, so the results are bitwise those of one thread per dim.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void combine_kernel(int C, int nt, int maxch,
-                                                    const int32_t* __restrict__ offsets,
-                                                    const int32_t* __restrict__ chunk_prefix,
-                                                    const float* __restrict__ partial, FPtr3 means,
-                                                    int mode, T* __restrict__ table,
-                                                    float* __restrict__ norms) {
-  __shared__ float wsum[2];
-  const int h = blockIdx.y, c = blockIdx.x, j = threadIdx.x;
+__global__ __launch_bounds__(256) void combine_kernel(int C, int nt, int maxch,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ chunk_prefix,
+                                                     const float* __restrict__ partial, FPtr3 means,
+                                                     int mode, T* __restrict__ table,
+                                                     float* __restrict__ norms) {
+  constexpr int EPL = D / 64;  // dims per lane
+  const int h = blockIdx.y, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= C) return;  // a whole wavefront; nothing below synchronises the block
   const int32_t* off = offsets + size_t(h) * (C + 1);
   const int32_t* cp = chunk_prefix + size_t(h) * (C + 1);
   const int n = off[c + 1] - off[c];
+  const int q0 = cp[c], q1 = cp[c + 1];
   for (int k = 0; k < nt; ++k) {
     float* mk = means.p[k];
-    float m;
-    if (n > 0) {
-      float s = 0.f;
-      for (int q = cp[c]; q < cp[c + 1]; ++q) s += partial[((size_t(h) * nt + k) * maxch + q) * D + j];
-      m = s / float(n);
-    } else {
-      m = (mode == 0 || !mk) ? 0.f : mk[(size_t(h) * C + c) * D + j];
+    float m[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int j = lane + 64 * e;
+      if (n > 0) {
+        float s = 0.f;
+        for (int q = q0; q < q1; ++q) s += partial[((size_t(h) * nt + k) * maxch + q) * D + j];
+        m[e] = s / float(n);
+      } else {
+        m[e] = (mode == 0 || !mk) ? 0.f : mk[(size_t(h) * C + c) * D + j];
+      }
+      if (mk) mk[(size_t(h) * C + c) * D + j] = m[e];
     }
-    if (mk) mk[(size_t(h) * C + c) * D + j] = m;
     if (k == 0 && table) {
-      const T r = from_f32<T>(m);
-      const float rf = to_f32(r);
-      table[(size_t(h) * C + c) * D + j] = from_f32<T>(-2.f * rf);
-      float sq = rf * rf;
-      for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-      if ((j & 63) == 0) wsum[j >> 6] = sq;
-      __syncthreads();
-      if (j == 0) norms[size_t(h) * C + c] = (D > 64) ? wsum[0] + wsum[1] : wsum[0];
-      __syncthreads();
+      float sq[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int j = lane + 64 * e;
+        const T r = from_f32<T>(m[e]);
+        const float rf = to_f32(r);
+        table[(size_t(h) * C + c) * D + j] = from_f32<T>(-2.f * rf);
+        sq[e] = rf * rf;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) sq[e] += __shfl_xor(sq[e], o, 64);
+      }
+      if (lane == 0) norms[size_t(h) * C + c] = (D > 64) ? sq[0] + sq[EPL - 1] : sq[0];
     }
   }
 }
@@ -349,7 +363,8 @@ static void combine_t(int H, int C, int nt, const int32_t* offsets, const int32_
                       float* norms, hipStream_t s) {
   FPtr3 mp{};
   for (int k = 0; k < nt; ++k) mp.p[k] = means ? means[k] : nullptr;
-  hipLaunchKernelGGL((combine_kernel<T, D>), dim3(C, H), dim3(D), 0, s, C, nt, max_chunks(N, C),
+  hipLaunchKernelGGL((combine_kernel<T, D>), dim3(ceil_div(C, 4), H), dim3(256), 0, s, C, nt,
+                     max_chunks(N, C),
                      offsets, cp, partial, mp, mode, static_cast<T*>(table), norms);
 }
 
