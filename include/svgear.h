@@ -23,6 +23,9 @@
  *   svgear_attend_unpermute  svgear_attend writing each output row at its
  *                    query's original position (§3.1, §4.1, §4.3)
  *
+ * and two measurement helpers outside the method: svgear_clock_probe and
+ * svgear_realtime_khz (the shader clock under matrix-core load).
+ *
  * Conventions shared by every call
  * --------------------------------
  *  - Tensors are DEVICE pointers, row-major, head-major: X[h][n][j] at
